@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Dispatch + combine throughput on one MI355X, against the HBM roofline.
+
+A step is one pass of the hot path over one batch: route (top-k) -> dispatch
+(count, scan, place, scatter) -> combine (weighted gather-reduce).  The
+experts' grouped GEMM is not part of the path; its per-expert scalar stand-in
+runs once per buffer set before timing, so combine reads expert outputs that
+are really in HBM.  Inputs are seeded synthetic data of the workload's shape,
+resident in HBM before the timed region.
+
+Cold (headline): S buffer sets rotate so that the bytes touched between two
+uses of a set exceed twice the 256 MB Infinity Cache.  Warm: one set, reused
+(cache-assisted), reported alongside.
+
+Timing: HIP graphs of back-to-back launches replayed between HIP events on the
+launch stream.  The step figure captures K whole steps; each kernel's average
+launch duration comes from a graph of K launches of that kernel alone.
+
+Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E peak
+MALL_BYTES = 256 << 20     # Infinity Cache
+METRIC = "dispatch+combine µs and HBM GB/s (% peak), DeepSeek-V3 shape, 128 tok/rank"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dsv3_decode")
+    ap.add_argument("--sets", type=int, default=0, help="cold buffer sets (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-warm", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (PMC scale factor)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes per launch (what the method must move)
+# ---------------------------------------------------------------------------
+def algorithmic_bytes(w):
+    T, H, E, k = w.T, w.H, w.E, w.k
+    if w.payload == "fp8":
+        row = H + 4 * (H // 128)
+        dispatch = T * (2 * H + k * row + 8 * k)
+        combine = T * (k * row + 8 * k + 2 * H)
+    else:
+        dispatch = T * (2 * H + 2 * H * k + 8 * k)
+        combine = T * (2 * H * k + 8 * k + 2 * H)
+    route = T * (4 * E + 8 * k) + (4 * E if w.zipf > 0 else 0)
+    return {"route": route, "dispatch": dispatch, "combine": combine}
+
+
+def source_sha():
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "combine_moe_dispatch_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "moe_dispatch.h"))
+    for f in files:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, kernel):
+    """HBM bytes per launch from a committed PMC summary, if it was taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("source_sha") != source_sha():
+        return None
+    val = kv.get(f"{kernel}_traffic_bytes_per_launch")
+    return None if val is None else float(val)
+
+
+# ---------------------------------------------------------------------------
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 5}), flush=True)
+
+
+class BufferSet:
+    def __init__(self, api, w, shape, inp, torch, np):
+        dev = "cuda"
+        self.logits = torch.from_numpy(inp.logits).to(dev)
+        self.bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
+        self.x = torch.from_numpy(inp.x_bits.view(np.int16).copy()).to(dev)
+        self.alpha = torch.from_numpy(inp.alpha).to(dev)
+        self.ids = torch.empty(w.T, w.k, dtype=torch.int32, device=dev)
+        self.w = torch.empty(w.T, w.k, dtype=torch.float32, device=dev)
+        self.lay = api.Layout.empty(shape, dev)
+        self.ws = api.alloc_workspace(shape, dev)
+        self.recv, self.rs = api.alloc_recv(shape, dev)
+        self.y, self.ys = api.alloc_recv(shape, dev)
+        self.out = torch.empty(w.T, w.H, dtype=torch.int16, device=dev)
+
+
+def run_gpu(args, w, inp):
+    import numpy as np
+    import torch
+
+    from combine_moe_dispatch_amd import api
+
+    torch.cuda.set_device(0)
+    shape = api.Shape(w.T, w.H, w.E, w.k, w.N, w.C,
+                      api.MOE_PAYLOAD_FP8_E4M3_B128 if w.payload == "fp8"
+                      else api.MOE_PAYLOAD_BF16)
+    nbytes = algorithmic_bytes(w)
+    per_step = nbytes["dispatch"] + nbytes["combine"] + nbytes["route"]
+    S = args.sets or max(2, math.ceil(2 * MALL_BYTES / per_step))
+    sets = [BufferSet(api, w, shape, inp, torch, np) for _ in range(S)]
+    stream = torch.cuda.Stream()
+
+    def route(s):
+        api.moe_route_topk(s.logits, s.bias, w.k, w.score, s.ids, s.w, stream=stream)
+
+    def dispatch(s):
+        api.moe_dispatch(shape, s.x, s.ids, s.recv, s.rs, s.lay, s.ws, stream=stream)
+
+    def combine(s):
+        api.moe_combine(shape, s.y, s.ys, s.lay, s.w, s.out, stream=stream)
+
+    def step(s):
+        route(s)
+        dispatch(s)
+        combine(s)
+
+    with torch.cuda.stream(stream):
+        for s in sets:   # layout + expert outputs for every set (untimed)
+            route(s)
+            dispatch(s)
+            api.moe_expert_scale(shape, s.recv, s.rs, s.lay, s.alpha, s.y, s.ys, stream=stream)
+            combine(s)
+    stream.synchronize()
+    status = int(sets[0].lay.status.item())
+
+    def capture(fn_list, n, rotate):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                s = sets[i % len(sets)] if rotate else sets[0]
+                for fn in fn_list:
+                    fn(s)
+        return g
+
+    def time_graph(g, n):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n  # us per unit
+
+    K, W = args.steps, args.warmup
+    res = {"sets": S, "status": status}
+    for mode, rotate in (("cold", True), ("warm", False)):
+        if mode == "warm" and args.no_warm:
+            continue
+        # warm-up: W eager steps, then one replay of each graph
+        with torch.cuda.stream(stream):
+            for i in range(W):
+                step(sets[i % len(sets)] if rotate else sets[0])
+        stream.synchronize()
+        g_step = capture([route, dispatch, combine], K, rotate)
+        g_route = capture([route], K, rotate)
+        g_disp = capture([dispatch], K, rotate)
+        g_comb = capture([combine], K, rotate)
+        for g in (g_step, g_route, g_disp, g_comb):
+            g.replay()
+        torch.cuda.synchronize()
+        step_us = time_graph(g_step, K)
+        r = {
+            "step_us": step_us,
+            "route_us": time_graph(g_route, K),
+            "dispatch_us": time_graph(g_disp, K),
+            "combine_us": time_graph(g_comb, K),
+        }
+        res[mode] = r
+        del g_step, g_route, g_disp, g_comb
+    return res
+
+
+def cpu_baseline(w, inp, seconds):
+    """The C oracle as it stands, single-threaded, on full steps of the same
+    workload until about `seconds` of work; dispatch and combine timed apart."""
+    import ctypes
+
+    import numpy as np
+
+    import oracle
+    lib = oracle._load()
+    ids, wt = oracle.route_topk(inp.logits, inp.bias, w.k, w.score)
+    lay = oracle.layout(ids, w.E, w.N, w.C)
+    rows = lay["rows"]
+    tr = np.ascontiguousarray(lay["token_row"])
+    x = np.ascontiguousarray(inp.x_bits)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    fp8 = w.payload == "fp8"
+    if fp8:
+        recv = np.zeros((rows, w.H), np.uint8)
+        rs = np.zeros((rows, w.H // 128), np.float32)
+    else:
+        recv = np.zeros((rows, w.H), np.uint16)
+        rs = None
+    out = np.empty((w.T, w.H), np.uint16)
+    td = tc = 0.0
+    reps = 0
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        if fp8:
+            lib.oracle_dispatch_fp8(p(x), w.T, w.H, w.k, p(tr), p(recv), p(rs))
+        else:
+            lib.oracle_dispatch_bf16(p(x), w.T, w.H, w.k, p(tr), p(recv))
+        t1 = time.perf_counter()
+        lib.oracle_combine_exact(p(recv), None if rs is None else p(rs), p(tr), p(wt), w.T,
+                                 w.k, w.H, p(out))
+        t2 = time.perf_counter()
+        td += t1 - t0
+        tc += t2 - t1
+        reps += 1
+        if time.perf_counter() - t_start >= seconds:
+            break
+    nbytes = algorithmic_bytes(w)
+    gbs = (nbytes["dispatch"] + nbytes["combine"]) * reps / (td + tc) / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full {w.name} steps (oracle dispatch + double-precision combine, "
+                      f"C, one thread); {1e6 * td / reps:.0f} us dispatch + "
+                      f"{1e6 * tc / reps:.0f} us combine per step",
+            "host": platform.processor() or platform.machine(),
+            "nproc": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the expert-parallel world; "
+              f"--gpus {args.gpus} is not supported (multi-GPU dispatch is not built).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    from combine_moe_dispatch_amd import inputs
+    w = inputs.WORKLOADS[args.workload]
+    inp = inputs.generate_for(w)
+    print(f"[bench] workload {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} N={w.N} C={w.C} "
+          f"payload={w.payload}", file=sys.stderr, flush=True)
+    g = run_gpu(args, w, inp)
+    print(f"[bench] gpu timing done: {json.dumps(g)}", file=sys.stderr, flush=True)
+    nbytes = algorithmic_bytes(w)
+    cold = g["cold"]
+    dc_us = cold["dispatch_us"] + cold["combine_us"]
+    dc_bytes = nbytes["dispatch"] + nbytes["combine"]
+    value = dc_bytes / (dc_us * 1e-6) / 1e9
+    dom = "dispatch" if cold["dispatch_us"] >= cold["combine_us"] else "combine"
+    dom_us = cold[f"{dom}_us"]
+    achieved = nbytes[dom] / (dom_us * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(cold["step_us"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.payload == "bf16" else "fp8-e4m3",
+        "data": "synthetic (seeded N(0,1) logits and tokens of the workload's shape)",
+        "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E,
+                   "top_k": w.k, "ranks": w.N, "rank_capacity": w.C, "payload": w.payload,
+                   "parallelism": "one source rank, N virtual destination ranks in HBM",
+                   "cold_buffer_sets": g["sets"]},
+        "dispatch_us": round(cold["dispatch_us"], 3),
+        "combine_us": round(cold["combine_us"], 3),
+        "dispatch_plus_combine_us": round(dc_us, 3),
+        "route_us": round(cold["route_us"], 3),
+        "step_us": round(cold["step_us"], 3),
+        "hbm_frac_dispatch_plus_combine": round(value / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic(w.name, dom)},
+        "device_status": g["status"],
+    }
+    if "warm" in g:
+        wm = g["warm"]
+        wus = wm["dispatch_us"] + wm["combine_us"]
+        line["warm_cache_assisted"] = {
+            "dispatch_us": round(wm["dispatch_us"], 3), "combine_us": round(wm["combine_us"], 3),
+            "route_us": round(wm["route_us"], 3), "step_us": round(wm["step_us"], 3),
+            "GBps": round(dc_bytes / (wus * 1e-6) / 1e9, 2)}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+"""Thin ctypes binding over libmoe_dispatch.so.
+
+Argument marshalling only: every step of routing, dispatch and combine runs in
+the library's HIP kernels.  torch supplies device memory and the stream.  The
+names and arguments follow the C ABI in include/moe_dispatch.h.  Importing this
+module loads the library and raises ImportError when it has not been built
+(``python -m combine_moe_dispatch_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_dispatch.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m combine_moe_dispatch_amd.build` (hipcc, gfx950)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_PAYLOAD_BF16, MOE_PAYLOAD_FP8_E4M3_B128 = 0, 1
+MOE_DEV_CAPACITY, MOE_DEV_BAD_ID = 1, 2
+MOE_MAX_EXPERTS, MOE_MAX_TOP_K = 1024, 32
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("num_ranks", ctypes.c_int32), ("rank_capacity", ctypes.c_int32),
+                ("payload", ctypes.c_int32)]
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "expert_counts", "expert_offsets", "rank_counts", "rank_offsets",
+        "token_row", "row_src", "status")]
+
+
+_vp, _i32 = ctypes.c_void_p, ctypes.c_int32
+_lib.moe_recv_rows.argtypes = [ctypes.POINTER(_Shape)]
+_lib.moe_recv_rows.restype = ctypes.c_int64
+_lib.moe_dispatch_workspace_size.argtypes = [ctypes.POINTER(_Shape)]
+_lib.moe_dispatch_workspace_size.restype = ctypes.c_size_t
+_lib.moe_route_topk.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+_lib.moe_route_topk.restype = _i32
+_lib.moe_dispatch.argtypes = [ctypes.POINTER(_Shape), _vp, _vp, _vp, _vp,
+                              ctypes.POINTER(_Layout), _vp, ctypes.c_size_t, _vp]
+_lib.moe_dispatch.restype = _i32
+_lib.moe_expert_scale.argtypes = [ctypes.POINTER(_Shape), _vp, _vp, ctypes.POINTER(_Layout),
+                                  _vp, _vp, _vp, _vp]
+_lib.moe_expert_scale.restype = _i32
+_lib.moe_combine.argtypes = [ctypes.POINTER(_Shape), _vp, _vp, ctypes.POINTER(_Layout),
+                             _vp, _vp, _vp]
+_lib.moe_combine.restype = _i32
+_lib.moe_status_string.argtypes = [_i32]
+_lib.moe_status_string.restype = ctypes.c_char_p
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {_lib.moe_status_string(status).decode()}")
+
+
+def _check(status: int, call: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, call)
+
+
+@dataclasses.dataclass(frozen=True)
+class Shape:
+    """Sizes of one problem (mirrors moe_shape)."""
+    num_tokens: int
+    hidden: int
+    num_experts: int
+    top_k: int
+    num_ranks: int
+    rank_capacity: int   # 0 = packed regions
+    payload: int = MOE_PAYLOAD_BF16
+
+    def c(self) -> _Shape:
+        return _Shape(self.num_tokens, self.hidden, self.num_experts, self.top_k,
+                      self.num_ranks, self.rank_capacity, self.payload)
+
+    @property
+    def fp8(self) -> bool:
+        return self.payload == MOE_PAYLOAD_FP8_E4M3_B128
+
+
+@dataclasses.dataclass
+class Layout:
+    """Device metadata tensors (mirrors moe_layout); row_src may be None."""
+    expert_counts: torch.Tensor
+    expert_offsets: torch.Tensor
+    rank_counts: torch.Tensor
+    rank_offsets: torch.Tensor
+    token_row: torch.Tensor
+    row_src: Optional[torch.Tensor]
+    status: torch.Tensor
+
+    def c(self) -> _Layout:
+        p = lambda t: None if t is None else t.data_ptr()
+        return _Layout(p(self.expert_counts), p(self.expert_offsets), p(self.rank_counts),
+                       p(self.rank_offsets), p(self.token_row), p(self.row_src), p(self.status))
+
+    @staticmethod
+    def empty(shape: Shape, device, with_row_src: bool = False) -> "Layout":
+        i = dict(dtype=torch.int32, device=device)
+        rows = moe_recv_rows(shape)
+        return Layout(torch.empty(shape.num_experts, **i), torch.empty(shape.num_experts, **i),
+                      torch.empty(shape.num_ranks, **i), torch.empty(shape.num_ranks, **i),
+                      torch.empty(shape.num_tokens, shape.top_k, **i),
+                      torch.full((rows,), -1, **i) if with_row_src else None,
+                      torch.zeros(1, **i))
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def moe_recv_rows(shape: Shape) -> int:
+    n = _lib.moe_recv_rows(ctypes.byref(shape.c()))
+    if n < 0:
+        raise MoeError(MOE_ERR_INVALID_ARG, "moe_recv_rows")
+    return int(n)
+
+
+def moe_dispatch_workspace_size(shape: Shape) -> int:
+    return int(_lib.moe_dispatch_workspace_size(ctypes.byref(shape.c())))
+
+
+def moe_route_topk(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int, score: int,
+                   topk_ids: Optional[torch.Tensor] = None,
+                   topk_weights: Optional[torch.Tensor] = None, stream=None):
+    """Top-k routing; returns (topk_ids int32 [T,k], topk_weights fp32 [T,k])."""
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    if topk_weights is None:
+        topk_weights = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _check(_lib.moe_route_topk(_ptr(logits), _ptr(bias), T, E, k, score, _ptr(topk_ids),
+                               _ptr(topk_weights), _stream(stream)), "moe_route_topk")
+    return topk_ids, topk_weights
+
+
+def moe_dispatch(shape: Shape, x: torch.Tensor, topk_ids: torch.Tensor, recv_x: torch.Tensor,
+                 recv_scales: Optional[torch.Tensor], layout: Layout,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.moe_dispatch(ctypes.byref(shape.c()), _ptr(x), _ptr(topk_ids), _ptr(recv_x),
+                             _ptr(recv_scales), ctypes.byref(layout.c()), _ptr(workspace),
+                             ws_bytes, _stream(stream)), "moe_dispatch")
+
+
+def moe_expert_scale(shape: Shape, recv_x: torch.Tensor, recv_scales: Optional[torch.Tensor],
+                     layout: Layout, alpha: torch.Tensor, y: torch.Tensor,
+                     y_scales: Optional[torch.Tensor], stream=None) -> None:
+    _check(_lib.moe_expert_scale(ctypes.byref(shape.c()), _ptr(recv_x), _ptr(recv_scales),
+                                 ctypes.byref(layout.c()), _ptr(alpha), _ptr(y), _ptr(y_scales),
+                                 _stream(stream)), "moe_expert_scale")
+
+
+def moe_combine(shape: Shape, expert_y: torch.Tensor, expert_scales: Optional[torch.Tensor],
+                layout: Layout, topk_weights: torch.Tensor, out: torch.Tensor,
+                stream=None) -> None:
+    _check(_lib.moe_combine(ctypes.byref(shape.c()), _ptr(expert_y), _ptr(expert_scales),
+                            ctypes.byref(layout.c()), _ptr(topk_weights), _ptr(out),
+                            _stream(stream)), "moe_combine")
+
+
+def moe_status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+def alloc_recv(shape: Shape, device, fill: Optional[int] = None):
+    """Receive buffer (bf16 rows or e4m3 codes) and, for fp8, its scales."""
+    rows = moe_recv_rows(shape)
+    if shape.fp8:
+        buf = torch.empty(rows, shape.hidden, dtype=torch.uint8, device=device)
+        sc = torch.empty(rows, shape.hidden // 128, dtype=torch.float32, device=device)
+    else:
+        buf = torch.empty(rows, shape.hidden, dtype=torch.int16, device=device)
+        sc = None
+    if fill is not None:
+        buf.fill_(fill if shape.fp8 else (fill - 0x10000 if fill >= 0x8000 else fill))
+        if sc is not None:
+            sc.fill_(float("nan"))
+    return buf, sc
+
+
+def alloc_workspace(shape: Shape, device) -> Optional[torch.Tensor]:
+    n = moe_dispatch_workspace_size(shape)
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)

@@ -1,0 +1,160 @@
+// capi.hip -- the C ABI of libmoe_dispatch.so: argument checks, then launches
+// on the caller's stream.  No allocation, no synchronisation, no state.
+#include "../../include/moe_dispatch.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates a shape; on success fills L and the receive row count.
+moe_status check_shape(const moe_shape* s, int* L, int64_t* rows) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->num_tokens < 0 || s->hidden <= 0 || s->num_experts < 1 || s->top_k < 1 ||
+      s->num_ranks < 1 || s->rank_capacity < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s->payload != MOE_PAYLOAD_BF16 && s->payload != MOE_PAYLOAD_FP8_E4M3_B128)
+    return MOE_ERR_INVALID_ARG;
+  if (s->top_k > s->num_experts) return MOE_ERR_INVALID_ARG;
+  if (s->num_experts % s->num_ranks != 0) return MOE_ERR_INVALID_ARG;
+  if (s->num_experts > MOE_MAX_EXPERTS || s->top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
+  if (s->payload == MOE_PAYLOAD_BF16 && s->hidden % 8 != 0) return MOE_ERR_INVALID_ARG;
+  if (s->payload == MOE_PAYLOAD_FP8_E4M3_B128 && s->hidden % 128 != 0) return MOE_ERR_INVALID_ARG;
+  const int64_t pairs = (int64_t)s->num_tokens * s->top_k;
+  const int64_t r = s->rank_capacity > 0 ? (int64_t)s->num_ranks * s->rank_capacity : pairs;
+  if (pairs > INT32_MAX || r > INT32_MAX) return MOE_ERR_UNSUPPORTED;  // rows are int32
+  *L = s->num_experts / s->num_ranks;
+  *rows = r;
+  return MOE_OK;
+}
+
+moe_status check_layout(const moe_layout* lay) {
+  if (!lay || !lay->expert_counts || !lay->expert_offsets || !lay->rank_counts ||
+      !lay->rank_offsets || !lay->token_row || !lay->status)
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_recv_rows(const moe_shape* shape) {
+  int L;
+  int64_t rows;
+  if (check_shape(shape, &L, &rows) != MOE_OK) return -1;
+  return rows;
+}
+
+size_t moe_dispatch_workspace_size(const moe_shape* shape) {
+  int L;
+  int64_t rows;
+  if (check_shape(shape, &L, &rows) != MOE_OK) return 0;
+  return moe::dispatch_workspace_bytes(shape->num_tokens, shape->top_k, shape->num_experts);
+}
+
+moe_status moe_route_topk(const float* logits, const float* bias, int32_t T, int32_t E,
+                          int32_t k, int32_t score, int32_t* topk_ids, float* topk_weights,
+                          hipStream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!logits || !topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)T * E > INT32_MAX * (int64_t)64) return MOE_ERR_UNSUPPORTED;
+  return from_hip(moe::launch_route_topk(logits, bias, T, E, k, score, topk_ids, topk_weights,
+                                         stream));
+}
+
+moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids,
+                        void* recv_x, float* recv_scales, const moe_layout* layout,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int L;
+  int64_t rows;
+  moe_status st = check_shape(shape, &L, &rows);
+  if (st != MOE_OK) return st;
+  if ((st = check_layout(layout)) != MOE_OK) return st;
+  const bool fp8 = shape->payload == MOE_PAYLOAD_FP8_E4M3_B128;
+  if (shape->num_tokens > 0) {
+    if (!x || !topk_ids || !recv_x) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(recv_x)) return MOE_ERR_INVALID_ARG;
+    if (fp8 && !recv_scales) return MOE_ERR_INVALID_ARG;
+  }
+  const size_t need = moe::dispatch_workspace_bytes(shape->num_tokens, shape->top_k,
+                                                    shape->num_experts);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return MOE_ERR_INVALID_ARG;
+
+  moe::DispatchParams p{};
+  p.x = x;
+  p.ids = topk_ids;
+  p.recv = recv_x;
+  p.recv_scales = recv_scales;
+  p.expert_counts = layout->expert_counts;
+  p.expert_offsets = layout->expert_offsets;
+  p.rank_counts = layout->rank_counts;
+  p.rank_offsets = layout->rank_offsets;
+  p.token_row = layout->token_row;
+  p.row_src = layout->row_src;
+  p.status = layout->status;
+  p.workspace = workspace;
+  p.T = shape->num_tokens;
+  p.H = shape->hidden;
+  p.E = shape->num_experts;
+  p.k = shape->top_k;
+  p.N = shape->num_ranks;
+  p.L = L;
+  p.C = shape->rank_capacity;
+  p.payload = fp8 ? 1 : 0;
+  return from_hip(moe::launch_dispatch(p, stream));
+}
+
+moe_status moe_expert_scale(const moe_shape* shape, const void* recv_x, const float* recv_scales,
+                            const moe_layout* layout, const float* alpha, void* y,
+                            float* y_scales, hipStream_t stream) {
+  int L;
+  int64_t rows;
+  moe_status st = check_shape(shape, &L, &rows);
+  if (st != MOE_OK) return st;
+  if (!layout || !layout->expert_counts || !layout->expert_offsets) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = shape->payload == MOE_PAYLOAD_FP8_E4M3_B128;
+  if (!recv_x || !y || !alpha || !aligned16(recv_x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  if (fp8 && (!recv_scales || !y_scales)) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_expert_scale(recv_x, recv_scales, layout->expert_counts,
+                                           layout->expert_offsets, alpha, y, y_scales,
+                                           shape->num_experts, L, shape->rank_capacity,
+                                           shape->hidden, fp8 ? 1 : 0, stream));
+}
+
+moe_status moe_combine(const moe_shape* shape, const void* expert_y, const float* expert_scales,
+                       const moe_layout* layout, const float* topk_weights, void* out,
+                       hipStream_t stream) {
+  int L;
+  int64_t rows;
+  moe_status st = check_shape(shape, &L, &rows);
+  if (st != MOE_OK) return st;
+  const bool fp8 = shape->payload == MOE_PAYLOAD_FP8_E4M3_B128;
+  if (shape->num_tokens > 0) {
+    if (!layout || !layout->token_row || !expert_y || !topk_weights || !out)
+      return MOE_ERR_INVALID_ARG;
+    if (!aligned16(expert_y) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+    if (fp8 && !expert_scales) return MOE_ERR_INVALID_ARG;
+  }
+  return from_hip(moe::launch_combine(expert_y, expert_scales,
+                                      layout ? layout->token_row : nullptr, topk_weights, out,
+                                      shape->num_tokens, shape->hidden, shape->top_k,
+                                      fp8 ? 1 : 0, stream));
+}
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null pointer, bad size or misaligned buffer";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside the library's limits";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+  }
+  return "unknown moe_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// device_common.h -- small device helpers shared by the kernels of
+// libmoe_dispatch.so: number-format conversions written from the formats,
+// wavefront primitives for wave64, and the launch limits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kMaxExperts = 1024;  // LDS histograms are sized for this
+constexpr int kMaxTopK = 32;
+constexpr int kFp8Block = 128;     // columns per fp8 scale
+
+// bf16 (8 exponent bits, 7 mantissa bits) from fp32, round to nearest even.
+// NaN stays NaN (quiet).  Pure integer arithmetic on the bit pattern.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// OCP e4m3fn code from an fp32 value: round to nearest even, magnitudes at or
+// beyond 448 saturate to 448 (code 0x7E), NaN gives 0x7F.
+//  - |v| < 2^-6 is subnormal in e4m3: the code is |v| / 2^-9 rounded to an
+//    integer (0..8; 8 is the smallest normal, code 0x08).
+//  - otherwise keep 3 mantissa bits of the fp32 pattern with RNE on the 20
+//    dropped bits and rebias the exponent from 127 to 7.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;  // >= 448
+  if (a < 0x3c800000u) {                      // < 2^-6
+    float m = rintf(__uint_as_float(a) * 512.0f);
+    return sign | (uint32_t)m;
+  }
+  a += 0x7ffffu + ((a >> 20) & 1u);
+  uint32_t code = (((a >> 23) - 120u) << 3) | ((a >> 20) & 7u);
+  return sign | code;
+}
+
+// fp32 value of an e4m3fn code (exact).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 24;
+  uint32_t e = (c >> 3) & 15u;
+  uint32_t m = c & 7u;
+  if ((c & 0x7fu) == 0x7fu) return __uint_as_float(0x7fc00000u | s);
+  if (e == 0) return __uint_as_float(s | __float_as_uint((float)m * 0.001953125f));
+  return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Inclusive/exclusive sums over a wave64 with shuffles.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+// Lanes of this wave whose `key` equals this lane's key (a 64-bit mask),
+// built one key bit at a time from ballots.  `bits` = number of key bits.
+__device__ __forceinline__ uint64_t wave_match(uint32_t key, int bits) {
+  uint64_t peers = ~0ull;
+  for (int b = 0; b < bits; ++b) {
+    uint32_t bit = (key >> b) & 1u;
+    uint64_t ones = __ballot(bit);
+    peers &= bit ? ones : ~ones;
+  }
+  return peers & __ballot(1);
+}
+
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+
+__device__ __forceinline__ uint64_t lanes_below() {
+  const int lane = lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace moe

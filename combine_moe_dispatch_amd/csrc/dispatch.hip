@@ -1,0 +1,467 @@
+// dispatch.hip -- MoE dispatch: count, scan, stable placement and scatter.
+//
+// What is computed ("Enabling trillion-parameter models on AWS EFA", sections
+// Send and Receive Buffers and Dispatch and Combine): per-expert token counts,
+// their cumulative sum giving the offset of each contiguous region, and the
+// token rows packed into those regions.  Expert e lives on rank e / L.  Inside
+// a rank's region the expert segments are ascending, and inside a segment the
+// (token, slot) pairs are ascending, so the placement never depends on the
+// order in which threads happen to run.
+//
+// The pages count with shared-memory atomics in a single block and then pack
+// send buffers for a network write.  Here the receive regions are in this
+// GPU's memory, so the pack is the final store, and the layout is derived
+// without any order-dependent atomics:
+//   row(t, j) = base(rank) + #{pairs of the rank with a smaller expert}
+//               + #{earlier pairs (t', j') < (t, j) with the same expert}.
+//
+// Two paths:
+//  * fused (T*k <= kSmallMaxPairs): one launch.  Block 0 builds the global
+//    histogram and scan and writes the metadata; every other block owns one
+//    (token, column chunk), keeps the whole id list in registers (a few ids
+//    per thread), obtains its token's k rows from three ballot-counted
+//    predicates over all ids, and stores its slice of the row k times.  The
+//    token's source vectors are loaded before the counting so that their
+//    latency overlaps it.
+//  * chunked (larger T*k): (1) per chunk of 1024 pairs, a block computes each
+//    pair's rank among equal experts inside the chunk (wave ballot matching,
+//    no atomics on the placement path) and the chunk's histogram; (2) one
+//    block turns the chunk histograms into per-chunk bases and the global
+//    metadata; (3) the scatter reads a pair's row from those.
+//
+// Rows move as 16-byte vectors; with the fp8 payload each group of 16 lanes
+// owns one 128-column block, reduces its amax with in-group shuffles and
+// stores 8 codes per lane plus one scale per block and destination.
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / kWave;
+constexpr int kIdsPerThread = kSmallMaxPairs / kBlock;  // 16
+constexpr int kDevCapacity = 1;
+constexpr int kDevBadId = 2;
+
+// Exclusive scan of n <= kMaxExperts LDS counts into excl[0..n] (excl[n] is
+// the total).  All threads of the block must call it.
+__device__ void block_exclusive_scan(const int* cnt, int n, int* excl, int* wave_tot) {
+  const int per = (n + kBlock - 1) / kBlock;
+  const int start = threadIdx.x * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (start + i < n) local += cnt[start + i];
+  const int incl = wave_inclusive_sum(local);
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == kWave - 1) wave_tot[w] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int i = 0; i < w; ++i) run += wave_tot[i];
+  for (int i = 0; i < per; ++i)
+    if (start + i < n) {
+      excl[start + i] = run;
+      run += cnt[start + i];
+    }
+  if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int i = 0; i < kWaves; ++i) tot += wave_tot[i];
+    excl[n] = tot;
+  }
+  __syncthreads();
+}
+
+// Global metadata from the per-expert counts and their exclusive scan.
+__device__ void write_metadata(const DispatchParams& p, const int* cnt, const int* excl,
+                               bool bad) {
+  for (int e = threadIdx.x; e < p.E; e += kBlock) {
+    const int r = e / p.L;
+    const int first = excl[r * p.L];
+    const int base = p.C > 0 ? r * p.C : first;
+    p.expert_counts[e] = cnt[e];
+    p.expert_offsets[e] = base + excl[e] - first;
+  }
+  bool over = false;
+  for (int r = threadIdx.x; r < p.N; r += kBlock) {
+    const int rc = excl[(r + 1) * p.L] - excl[r * p.L];
+    p.rank_counts[r] = rc;
+    p.rank_offsets[r] = p.C > 0 ? r * p.C : excl[r * p.L];
+    if (p.C > 0 && rc > p.C) over = true;
+  }
+  over = __syncthreads_or(over);
+  if (threadIdx.x == 0) *p.status = (bad ? kDevBadId : 0) | (over ? kDevCapacity : 0);
+}
+
+// ---------------------------------------------------------------------------
+// Scatter of one token's column slice to its k destination rows.
+// ---------------------------------------------------------------------------
+template <int MAXV>
+__device__ __forceinline__ void load_slice(const DispatchParams& p, int t, int v0, int v1,
+                                           uint4 (&xv)[MAXV]) {
+  const int nvec = p.H / 8;
+  const uint4* x = reinterpret_cast<const uint4*>(p.x) + (size_t)t * nvec;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int v = v0 + threadIdx.x + i * kBlock;
+    xv[i] = v < v1 ? x[v] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int MAXV>
+__device__ __forceinline__ void store_bf16(const DispatchParams& p, int v0, int v1,
+                                           const uint4 (&xv)[MAXV], const int* s_row) {
+  const int nvec = p.H / 8;
+  uint4* recv = reinterpret_cast<uint4*>(p.recv);
+  for (int j = 0; j < p.k; ++j) {
+    const int row = s_row[j];
+    if (row < 0) continue;
+    uint4* dst = recv + (size_t)row * nvec;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int v = v0 + threadIdx.x + i * kBlock;
+      if (v < v1) dst[v] = xv[i];
+    }
+  }
+}
+
+// fp8: a vector is 8 columns; 16 consecutive lanes hold one 128-column block
+// (v0 and v1 are multiples of 16, so a group is all in or all out).
+template <int MAXV>
+__device__ __forceinline__ void store_fp8(const DispatchParams& p, int v0, int v1,
+                                          const uint4 (&xv)[MAXV], const int* s_row) {
+  const int nb = p.H / kFp8Block;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int v = v0 + threadIdx.x + i * kBlock;
+    if (v >= v1) continue;
+    float f[8];
+    const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      f[2 * m] = bf16_lo(w4[m]);
+      f[2 * m + 1] = bf16_hi(w4[m]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) amax = fmaxf(amax, fabsf(f[m]));
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, kWave));
+    const float s = amax / 448.0f;
+    uint32_t lo = 0, hi = 0;
+    if (amax != 0.0f) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) lo |= f32_to_e4m3(f[m] / s) << (8 * m);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) hi |= f32_to_e4m3(f[4 + m] / s) << (8 * m);
+    }
+    for (int j = 0; j < p.k; ++j) {
+      const int row = s_row[j];
+      if (row < 0) continue;
+      uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(p.recv) + (size_t)row * p.H);
+      dst[v] = make_uint2(lo, hi);
+      if ((threadIdx.x & 15) == 0) p.recv_scales[(size_t)row * nb + v / 16] = s;
+    }
+  }
+}
+
+__device__ __forceinline__ void publish_rows(const DispatchParams& p, int t, int cc,
+                                             const int* s_row) {
+  if (cc == 0 && threadIdx.x < p.k) {
+    const int q = t * p.k + threadIdx.x;
+    const int row = s_row[threadIdx.x];
+    p.token_row[q] = row;
+    if (p.row_src && row >= 0) p.row_src[row] = q;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused single-launch path.
+// ---------------------------------------------------------------------------
+template <int PAYLOAD, int MAXV>
+__global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p) {
+  __shared__ int s_a[kMaxExperts];
+  __shared__ int s_b[kMaxExperts + 1];
+  __shared__ int s_wave[kWaves];
+  __shared__ int s_row[kMaxTopK];
+  const int P = p.T * p.k;
+  const int tid = threadIdx.x;
+
+  if (blockIdx.x == 0) {
+    // histogram, scan and the global metadata
+    for (int e = tid; e < p.E; e += kBlock) s_a[e] = 0;
+    __syncthreads();
+    bool bad = false;
+    for (int q = tid; q < P; q += kBlock) {
+      const int e = p.ids[q];
+      if ((unsigned)e < (unsigned)p.E)
+        atomicAdd(&s_a[e], 1);
+      else
+        bad = true;
+    }
+    bad = __syncthreads_or(bad);
+    block_exclusive_scan(s_a, p.E, s_b, s_wave);
+    write_metadata(p, s_a, s_b, bad);
+    return;
+  }
+
+  const int b = blockIdx.x - 1;
+  const int t = b / p.col_chunks;
+  const int cc = b - t * p.col_chunks;
+  const int nvec = p.H / 8;
+  const int v0 = cc * p.vec_per_chunk;
+  const int v1 = min(v0 + p.vec_per_chunk, nvec);
+
+  // the id list, a few per thread, then this block's slice of the token
+  int idv[kIdsPerThread];
+#pragma unroll
+  for (int i = 0; i < kIdsPerThread; ++i) {
+    const int q = tid + i * kBlock;
+    idv[i] = q < P ? p.ids[q] : -1;
+  }
+  uint4 xv[MAXV];
+  load_slice<MAXV>(p, t, v0, v1, xv);
+
+  // For slot j with expert e: A = #valid ids < e, R = #valid ids below the
+  // first expert of e's rank, B = #ids == e at positions before t*k + j.
+  const int w = tid / kWave;
+  int* s_part = s_a;  // [kWaves][kMaxTopK][3]
+  for (int j = 0; j < p.k; ++j) {
+    const int pos = t * p.k + j;
+    const int e = p.ids[pos];
+    const unsigned ue = (unsigned)e;
+    const unsigned urb = (unsigned)((e / p.L) * p.L);
+    int a = 0, bb = 0, r = 0;
+#pragma unroll
+    for (int i = 0; i < kIdsPerThread; ++i) {
+      const int q = tid + i * kBlock;
+      if (i * kBlock < P) {  // uniform
+        const bool in = q < P;
+        const unsigned id = (unsigned)idv[i];
+        a += popc64(__ballot(in && id < ue));
+        bb += popc64(__ballot(in && id == ue && q < pos));
+        r += popc64(__ballot(in && id < urb));
+      }
+    }
+    if (lane_id() == 0) {
+      s_part[(w * kMaxTopK + j) * 3 + 0] = a;
+      s_part[(w * kMaxTopK + j) * 3 + 1] = bb;
+      s_part[(w * kMaxTopK + j) * 3 + 2] = r;
+    }
+  }
+  __syncthreads();
+  if (tid < p.k) {
+    const int j = tid;
+    int A = 0, B = 0, R = 0;
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      A += s_part[(w2 * kMaxTopK + j) * 3 + 0];
+      B += s_part[(w2 * kMaxTopK + j) * 3 + 1];
+      R += s_part[(w2 * kMaxTopK + j) * 3 + 2];
+    }
+    const int e = p.ids[t * p.k + j];
+    int row = -1;
+    if ((unsigned)e < (unsigned)p.E) {
+      if (p.C > 0) {
+        const int local = (A - R) + B;
+        if (local < p.C) row = (e / p.L) * p.C + local;
+      } else {
+        row = A + B;
+      }
+    }
+    s_row[j] = row;
+  }
+  __syncthreads();
+  publish_rows(p, t, cc, s_row);
+  if (PAYLOAD == 0)
+    store_bf16<MAXV>(p, v0, v1, xv, s_row);
+  else
+    store_fp8<MAXV>(p, v0, v1, xv, s_row);
+}
+
+// ---------------------------------------------------------------------------
+// Chunked path, kernel 1: ranks inside a chunk and the chunk's histogram.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kBlock) layout_chunk_kernel(DispatchParams p) {
+  __shared__ int s_run[kMaxExperts];
+  __shared__ int s_whist[kWaves][kMaxExperts];
+  constexpr int kSubs = kChunkPairs / kBlock;
+  const int c = blockIdx.x;
+  const int P = p.T * p.k;
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+
+  int idv[kSubs];
+#pragma unroll
+  for (int s = 0; s < kSubs; ++s) {
+    const int q = c * kChunkPairs + s * kBlock + tid;
+    idv[s] = q < P ? p.ids[q] : p.E;
+  }
+  for (int e = tid; e < p.E; e += kBlock) {
+    s_run[e] = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) s_whist[w2][e] = 0;
+  }
+  __syncthreads();
+
+  const int bits = 32 - __clz(p.E);  // keys 0..E, E marks "no valid id"
+  bool bad = false;
+#pragma unroll
+  for (int s = 0; s < kSubs; ++s) {
+    const int q = c * kChunkPairs + s * kBlock + tid;
+    const bool has = q < P;
+    const int e = idv[s];
+    const bool valid = has && (unsigned)e < (unsigned)p.E;
+    bad |= has && !valid;
+    const uint32_t key = valid ? (uint32_t)e : (uint32_t)p.E;
+    const uint64_t peers = wave_match(key, bits);
+    const int before = popc64(peers & lanes_below());
+    const int total = popc64(peers);
+    const bool last = before == total - 1;
+    if (valid && last) s_whist[w][e] = total;
+    __syncthreads();
+    if (valid) {
+      int pre = s_run[e];
+      for (int w2 = 0; w2 < w; ++w2) pre += s_whist[w2][e];
+      p.local_rank[q] = pre + before;
+    }
+    __syncthreads();
+    if (valid && last) {
+      atomicAdd(&s_run[e], total);  // sums are order-independent
+      s_whist[w][e] = 0;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < p.E; e += kBlock) p.chunk_hist[(size_t)c * p.E + e] = s_run[e];
+  bad = __syncthreads_or(bad);
+  if (tid == 0) p.chunk_bad[c] = bad ? 1 : 0;
+}
+
+// Chunked path, kernel 2: per-chunk bases (exclusive over chunks, in place),
+// global counts, scan and metadata.  One block.
+__global__ void __launch_bounds__(kBlock) layout_scan_kernel(DispatchParams p) {
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_excl[kMaxExperts + 1];
+  __shared__ int s_wave[kWaves];
+  constexpr int kBatch = 16;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < p.E; e += kBlock) {
+    int run = 0;
+    for (int c0 = 0; c0 < p.nchunks; c0 += kBatch) {
+      int h[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        h[i] = c0 + i < p.nchunks ? p.chunk_hist[(size_t)(c0 + i) * p.E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (c0 + i < p.nchunks) {
+          p.chunk_hist[(size_t)(c0 + i) * p.E + e] = run;
+          run += h[i];
+        }
+    }
+    s_cnt[e] = run;
+  }
+  bool bad = false;
+  for (int c = tid; c < p.nchunks; c += kBlock) bad |= p.chunk_bad[c] != 0;
+  bad = __syncthreads_or(bad);
+  block_exclusive_scan(s_cnt, p.E, s_excl, s_wave);
+  write_metadata(p, s_cnt, s_excl, bad);
+}
+
+// Chunked path, kernel 3: rows from the chunk bases, then the scatter.
+template <int PAYLOAD, int MAXV>
+__global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams p) {
+  __shared__ int s_row[kMaxTopK];
+  const int t = blockIdx.x / p.col_chunks;
+  const int cc = blockIdx.x - t * p.col_chunks;
+  const int nvec = p.H / 8;
+  const int v0 = cc * p.vec_per_chunk;
+  const int v1 = min(v0 + p.vec_per_chunk, nvec);
+  uint4 xv[MAXV];
+  load_slice<MAXV>(p, t, v0, v1, xv);
+  if (threadIdx.x < p.k) {
+    const int q = t * p.k + threadIdx.x;
+    const int e = p.ids[q];
+    int row = -1;
+    if ((unsigned)e < (unsigned)p.E) {
+      const int pos = p.chunk_hist[(size_t)(q / kChunkPairs) * p.E + e] + p.local_rank[q];
+      if (p.C > 0) {
+        const int r = e / p.L;
+        const int local = p.expert_offsets[e] - r * p.C + pos;
+        if (local < p.C) row = r * p.C + local;
+      } else {
+        row = p.expert_offsets[e] + pos;
+      }
+    }
+    s_row[threadIdx.x] = row;
+  }
+  __syncthreads();
+  publish_rows(p, t, cc, s_row);
+  if (PAYLOAD == 0)
+    store_bf16<MAXV>(p, v0, v1, xv, s_row);
+  else
+    store_fp8<MAXV>(p, v0, v1, xv, s_row);
+}
+
+template <int PAYLOAD, int MAXV>
+hipError_t launch_paths(const DispatchParams& p, hipStream_t st) {
+  const long P = (long)p.T * p.k;
+  if (P <= kSmallMaxPairs) {
+    const unsigned blocks = 1u + (unsigned)p.T * (unsigned)p.col_chunks;
+    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV>), dim3(blocks), dim3(kBlock), 0,
+                       st, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunks), dim3(kBlock), 0, st, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kBlock), 0, st, p);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((dispatch_scatter_kernel<PAYLOAD, MAXV>),
+                     dim3((unsigned)p.T * (unsigned)p.col_chunks), dim3(kBlock), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int PAYLOAD>
+hipError_t launch_payload(const DispatchParams& p, hipStream_t st) {
+  const int maxv = (p.vec_per_chunk + kBlock - 1) / kBlock;
+  if (maxv <= 1) return launch_paths<PAYLOAD, 1>(p, st);
+  if (maxv <= 2) return launch_paths<PAYLOAD, 2>(p, st);
+  return launch_paths<PAYLOAD, 4>(p, st);
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t dispatch_workspace_bytes(int T, int k, int E) {
+  const size_t P = (size_t)T * (size_t)k;
+  if (P <= (size_t)kSmallMaxPairs) return 0;
+  const size_t nch = (P + kChunkPairs - 1) / kChunkPairs;
+  return align256(4 * P) + align256(4 * nch * (size_t)E) + align256(4 * nch);
+}
+
+hipError_t launch_dispatch(const DispatchParams& in, hipStream_t st) {
+  DispatchParams p = in;
+  const int nvec = p.H / 8;
+  // column chunks of at most 256 vectors (one per thread), balanced, and a
+  // multiple of 16 vectors so an fp8 scale block never straddles two blocks
+  p.col_chunks = (nvec + kBlock - 1) / kBlock;
+  int vpc = (nvec + p.col_chunks - 1) / p.col_chunks;
+  vpc = (vpc + 15) / 16 * 16;
+  p.vec_per_chunk = vpc;
+  p.col_chunks = (nvec + vpc - 1) / vpc;
+  const size_t P = (size_t)p.T * p.k;
+  p.nchunks = (int)((P + kChunkPairs - 1) / kChunkPairs);
+  if (P > (size_t)kSmallMaxPairs) {
+    char* ws = reinterpret_cast<char*>(p.workspace);
+    p.local_rank = reinterpret_cast<int32_t*>(ws);
+    ws += align256(4 * P);
+    p.chunk_hist = reinterpret_cast<int32_t*>(ws);
+    ws += align256(4 * (size_t)p.nchunks * p.E);
+    p.chunk_bad = reinterpret_cast<int32_t*>(ws);
+  }
+  return p.payload == 0 ? launch_payload<0>(p, st) : launch_payload<1>(p, st);
+}
+
+}  // namespace moe

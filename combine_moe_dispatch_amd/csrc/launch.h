@@ -1,0 +1,54 @@
+// launch.h -- internal launchers of libmoe_dispatch.so (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Pairs up to which dispatch runs as one fused kernel: each block recounts
+// the whole id list from LDS, which stays cheap while it is this short.
+constexpr int kSmallMaxPairs = 4096;
+// Pairs per chunk of the multi-kernel layout path.
+constexpr int kChunkPairs = 1024;
+
+struct DispatchParams {
+  const void* x;
+  const int32_t* ids;
+  void* recv;
+  float* recv_scales;
+  int32_t* expert_counts;
+  int32_t* expert_offsets;
+  int32_t* rank_counts;
+  int32_t* rank_offsets;
+  int32_t* token_row;
+  int32_t* row_src;
+  int32_t* status;
+  void* workspace;      // multi-kernel path: carved into the three arrays below
+  int32_t* local_rank;  // [T*k] rank of a pair among equal experts in its chunk
+  int32_t* chunk_hist;  // [nchunks][E] chunk histograms, then chunk bases
+  int32_t* chunk_bad;   // [nchunks] chunk saw an id outside [0, E)
+  int T, H, E, k, N, L, C;
+  int payload;
+  int nchunks;
+  int col_chunks;     // blocks per token in the scatter
+  int vec_per_chunk;  // 16-byte source vectors per block
+};
+
+size_t dispatch_workspace_bytes(int T, int k, int E);
+hipError_t launch_dispatch(const DispatchParams& p, hipStream_t st);
+
+hipError_t launch_route_topk(const float* logits, const float* bias, int T, int E, int k,
+                             int score, int32_t* ids, float* w, hipStream_t st);
+
+hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_row,
+                          const float* w, void* out, int T, int H, int k, int payload,
+                          hipStream_t st);
+
+hipError_t launch_expert_scale(const void* recv, const float* recv_scales,
+                               const int32_t* expert_counts, const int32_t* expert_offsets,
+                               const float* alpha, void* y, float* y_scales, int E, int L,
+                               int C, int H, int payload, hipStream_t st);
+
+}  // namespace moe

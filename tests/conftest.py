@@ -10,4 +10,12 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    config.addinivalue_line("markers", "slow: larger CPU cases")
+    # Load what is built; build only when nothing is (hipcc cross-compiles on
+    # a CPU-only host too).
+    lib = os.path.join(ROOT, "combine_moe_dispatch_amd", "libmoe_dispatch.so")
+    if not os.path.exists(lib):
+        from combine_moe_dispatch_amd import build as _b
+        _b.build()
+    if not os.path.exists(os.path.join(ROOT, "oracle", "libmoe_oracle.so")):
+        import oracle
+        oracle.build()

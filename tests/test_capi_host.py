@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/moe_dispatch.h
+declares, and reject invalid arguments synchronously, before any launch --
+these paths touch no device, so they run on the CPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_dispatch.h")
+
+api = pytest.importorskip("combine_moe_dispatch_amd.api",
+                          reason="libmoe_dispatch.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("moe_route_topk", "moe_dispatch", "moe_combine", "moe_expert_scale",
+              "moe_recv_rows", "moe_dispatch_workspace_size", "moe_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(api.LIB_PATH)
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_recv_rows_and_workspace():
+    S = api.Shape
+    assert api.moe_recv_rows(S(128, 7168, 256, 8, 32, 1024)) == 32768
+    assert api.moe_recv_rows(S(4096, 7168, 256, 8, 32, 0)) == 32768
+    assert api.moe_recv_rows(S(0, 8, 1, 1, 1, 0)) == 0
+    assert api.moe_dispatch_workspace_size(S(128, 7168, 256, 8, 32, 1024)) == 0
+    assert api.moe_dispatch_workspace_size(S(512, 7168, 256, 8, 32, 4096, 1)) == 0
+    ws = api.moe_dispatch_workspace_size(S(4096, 7168, 256, 8, 32, 0))
+    assert ws >= 4 * 32768 + 4 * 32 * 256 + 4 * 32
+    with pytest.raises(api.MoeError):
+        api.moe_recv_rows(S(1, 8, 10, 2, 4, 0))  # E % N != 0
+
+
+@pytest.mark.parametrize("shape,code", [
+    ((4, 12, 8, 2, 2, 0, 0), 1),        # H % 8 != 0 for bf16
+    ((4, 64, 8, 2, 2, 0, 1), 1),        # H % 128 != 0 for fp8
+    ((4, 64, 8, 9, 2, 0, 0), 1),        # k > E
+    ((4, 64, 9, 2, 2, 0, 0), 1),        # E % N != 0
+    ((-1, 64, 8, 2, 2, 0, 0), 1),       # T < 0
+    ((4, 64, 8, 2, 2, -1, 0), 1),       # C < 0
+    ((4, 64, 8, 2, 2, 0, 7), 1),        # unknown payload
+    ((4, 64, 2048, 2, 2, 0, 0), 2),     # E beyond the LDS histogram
+    ((4, 64, 64, 33, 2, 0, 0), 2),      # k beyond MOE_MAX_TOP_K
+])
+def test_dispatch_rejects_bad_shapes(shape, code):
+    s = api._Shape(*shape)
+    lay = api._Layout(16, 16, 16, 16, 16, None, 16)
+    rc = api._lib.moe_dispatch(ctypes.byref(s), 16, 16, 16, 16, ctypes.byref(lay), None, 0, None)
+    assert rc == code
+    rc = api._lib.moe_combine(ctypes.byref(s), 16, 16, ctypes.byref(lay), 16, 16, None)
+    assert rc == code
+
+
+def test_dispatch_rejects_null_and_misaligned_pointers():
+    s = api._Shape(4, 64, 8, 2, 2, 0, 0)
+    good = api._Layout(16, 16, 16, 16, 16, None, 16)
+    f = api._lib.moe_dispatch
+    assert f(None, 16, 16, 16, None, ctypes.byref(good), None, 0, None) == 1
+    assert f(ctypes.byref(s), 16, 16, 16, None, None, None, 0, None) == 1
+    nostatus = api._Layout(16, 16, 16, 16, 16, None, None)
+    assert f(ctypes.byref(s), 16, 16, 16, None, ctypes.byref(nostatus), None, 0, None) == 1
+    assert f(ctypes.byref(s), 8, 16, 16, None, ctypes.byref(good), None, 0, None) == 1   # x
+    assert f(ctypes.byref(s), 16, 16, 24, None, ctypes.byref(good), None, 0, None) == 1  # recv
+    s8 = api._Shape(4, 128, 8, 2, 2, 0, 1)
+    assert f(ctypes.byref(s8), 16, 16, 16, None, ctypes.byref(good), None, 0, None) == 1  # scales
+    big = api._Shape(1000, 64, 8, 8, 2, 0, 0)  # needs a workspace
+    assert f(ctypes.byref(big), 16, 16, 16, None, ctypes.byref(good), None, 0, None) == 1
+    assert f(ctypes.byref(big), 16, 16, 16, None, ctypes.byref(good), 16, 8, None) == 1
+
+
+def test_combine_and_expert_scale_reject_bad_pointers():
+    s = api._Shape(4, 64, 8, 2, 2, 0, 0)
+    lay = api._Layout(16, 16, 16, 16, 16, None, 16)
+    c = api._lib.moe_combine
+    assert c(ctypes.byref(s), None, None, ctypes.byref(lay), 16, 16, None) == 1
+    assert c(ctypes.byref(s), 16, None, ctypes.byref(lay), 16, 8, None) == 1
+    assert c(ctypes.byref(s), 16, None, None, 16, 16, None) == 1
+    x = api._lib.moe_expert_scale
+    assert x(ctypes.byref(s), 16, None, ctypes.byref(lay), None, 16, None, None) == 1
+    s8 = api._Shape(4, 128, 8, 2, 2, 0, 1)
+    assert x(ctypes.byref(s8), 16, None, ctypes.byref(lay), 16, 16, None, None) == 1
+
+
+def test_route_rejects_bad_arguments():
+    r = api._lib.moe_route_topk
+    assert r(16, None, 4, 8, 9, 1, 16, 16, None) == 1      # k > E
+    assert r(16, None, 4, 8, 2, 5, 16, 16, None) == 1      # bad score
+    assert r(None, None, 4, 8, 2, 1, 16, 16, None) == 1    # null logits
+    assert r(16, None, 4, 2048, 2, 1, 16, 16, None) == 2   # E too large
+    assert r(16, None, -1, 8, 2, 1, 16, 16, None) == 1
+
+
+def test_status_strings():
+    for code in range(4):
+        assert api.moe_status_string(code).startswith("MOE_")
