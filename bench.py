@@ -175,12 +175,15 @@ def run_gpu(args, w, inp):
         return g
 
     def time_graph(g, n):
+        # replay() launches on torch's current stream: make that the launch
+        # stream, and bracket the replay with events recorded on it
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / n  # us per unit
 
@@ -198,8 +201,9 @@ def run_gpu(args, w, inp):
         g_route = capture([route], K, rotate)
         g_disp = capture([dispatch], K, rotate)
         g_comb = capture([combine], K, rotate)
-        for g in (g_step, g_route, g_disp, g_comb):
-            g.replay()
+        with torch.cuda.stream(stream):
+            for g in (g_step, g_route, g_disp, g_comb):
+                g.replay()
         torch.cuda.synchronize()
         step_us = time_graph(g_step, K)
         r = {

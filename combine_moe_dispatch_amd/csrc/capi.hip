@@ -28,9 +28,10 @@ moe_status check_shape(const moe_shape* s, int* L, int64_t* rows) {
   return MOE_OK;
 }
 
-moe_status check_layout(const moe_layout* lay) {
+// token_row may be NULL only when there are no tokens (an empty array).
+moe_status check_layout(const moe_layout* lay, int32_t T) {
   if (!lay || !lay->expert_counts || !lay->expert_offsets || !lay->rank_counts ||
-      !lay->rank_offsets || !lay->token_row || !lay->status)
+      !lay->rank_offsets || !lay->status || (T > 0 && !lay->token_row))
     return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
@@ -74,7 +75,7 @@ moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* to
   int64_t rows;
   moe_status st = check_shape(shape, &L, &rows);
   if (st != MOE_OK) return st;
-  if ((st = check_layout(layout)) != MOE_OK) return st;
+  if ((st = check_layout(layout, shape->num_tokens)) != MOE_OK) return st;
   const bool fp8 = shape->payload == MOE_PAYLOAD_FP8_E4M3_B128;
   if (shape->num_tokens > 0) {
     if (!x || !topk_ids || !recv_x) return MOE_ERR_INVALID_ARG;
@@ -119,7 +120,9 @@ moe_status moe_expert_scale(const moe_shape* shape, const void* recv_x, const fl
   if (st != MOE_OK) return st;
   if (!layout || !layout->expert_counts || !layout->expert_offsets) return MOE_ERR_INVALID_ARG;
   const bool fp8 = shape->payload == MOE_PAYLOAD_FP8_E4M3_B128;
-  if (!recv_x || !y || !alpha || !aligned16(recv_x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  if (!alpha) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;  // nothing can be placed
+  if (!recv_x || !y || !aligned16(recv_x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
   if (fp8 && (!recv_scales || !y_scales)) return MOE_ERR_INVALID_ARG;
   return from_hip(moe::launch_expert_scale(recv_x, recv_scales, layout->expert_counts,
                                            layout->expert_offsets, alpha, y, y_scales,

@@ -14,15 +14,17 @@
 // without any order-dependent atomics:
 //   row(t, j) = base(rank) + #{pairs of the rank with a smaller expert}
 //               + #{earlier pairs (t', j') < (t, j) with the same expert}.
+// (Histograms are built with LDS atomic adds, whose sums do not depend on the
+// order the adds land in.)
 //
 // Two paths:
 //  * fused (T*k <= kSmallMaxPairs): one launch.  Block 0 builds the global
 //    histogram and scan and writes the metadata; every other block owns one
-//    (token, column chunk), keeps the whole id list in registers (a few ids
-//    per thread), obtains its token's k rows from three ballot-counted
-//    predicates over all ids, and stores its slice of the row k times.  The
-//    token's source vectors are loaded before the counting so that their
-//    latency overlaps it.
+//    (token, column chunk).  It loads the whole id list (a few ids per
+//    thread) and its slice of the token row at once, builds two LDS
+//    histograms (all ids; ids before this token), lets one wave scan 64 chunk
+//    sums of the first, reads its k rows off them, and stores its slice of
+//    the row k times.
 //  * chunked (larger T*k): (1) per chunk of 1024 pairs, a block computes each
 //    pair's rank among equal experts inside the chunk (wave ballot matching,
 //    no atomics on the placement path) and the chunk's histogram; (2) one
@@ -180,24 +182,36 @@ __device__ __forceinline__ void publish_rows(const DispatchParams& p, int t, int
 // ---------------------------------------------------------------------------
 template <int PAYLOAD, int MAXV>
 __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p) {
-  __shared__ int s_a[kMaxExperts];
-  __shared__ int s_b[kMaxExperts + 1];
+  __shared__ int s_a[kMaxExperts];      // histogram of all ids
+  __shared__ int s_b[kMaxExperts + 1];  // block 0: scan; others: histogram before this token
   __shared__ int s_wave[kWaves];
+  __shared__ int s_chunk[kWave];        // exclusive prefix of 64 chunk sums of s_a
   __shared__ int s_row[kMaxTopK];
   const int P = p.T * p.k;
   const int tid = threadIdx.x;
+  const int lane = lane_id();
 
   if (blockIdx.x == 0) {
-    // histogram, scan and the global metadata
+    // histogram, scan and the global metadata; all id loads are issued
+    // before the first one is used
+    int idv[kIdsPerThread];
+#pragma unroll
+    for (int i = 0; i < kIdsPerThread; ++i) {
+      const int q = tid + i * kBlock;
+      idv[i] = q < P ? p.ids[q] : 0;
+    }
     for (int e = tid; e < p.E; e += kBlock) s_a[e] = 0;
     __syncthreads();
     bool bad = false;
-    for (int q = tid; q < P; q += kBlock) {
-      const int e = p.ids[q];
-      if ((unsigned)e < (unsigned)p.E)
-        atomicAdd(&s_a[e], 1);
-      else
-        bad = true;
+#pragma unroll
+    for (int i = 0; i < kIdsPerThread; ++i) {
+      if (tid + i * kBlock < P) {
+        const int e = idv[i];
+        if ((unsigned)e < (unsigned)p.E)
+          atomicAdd(&s_a[e], 1);
+        else
+          bad = true;
+      }
     }
     bad = __syncthreads_or(bad);
     block_exclusive_scan(s_a, p.E, s_b, s_wave);
@@ -212,7 +226,9 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   const int v0 = cc * p.vec_per_chunk;
   const int v1 = min(v0 + p.vec_per_chunk, nvec);
 
-  // the id list, a few per thread, then this block's slice of the token
+  // issue every load first: this token's k ids, the whole id list (a few
+  // per thread) and this block's slice of the token row
+  const int my_e = lane < p.k ? p.ids[t * p.k + lane] : -1;  // lane j: expert of slot j
   int idv[kIdsPerThread];
 #pragma unroll
   for (int i = 0; i < kIdsPerThread; ++i) {
@@ -222,53 +238,60 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   uint4 xv[MAXV];
   load_slice<MAXV>(p, t, v0, v1, xv);
 
-  // For slot j with expert e: A = #valid ids < e, R = #valid ids below the
-  // first expert of e's rank, B = #ids == e at positions before t*k + j.
-  const int w = tid / kWave;
-  int* s_part = s_a;  // [kWaves][kMaxTopK][3]
-  for (int j = 0; j < p.k; ++j) {
-    const int pos = t * p.k + j;
-    const int e = p.ids[pos];
-    const unsigned ue = (unsigned)e;
-    const unsigned urb = (unsigned)((e / p.L) * p.L);
-    int a = 0, bb = 0, r = 0;
+  // two histograms: all ids, and ids at positions before this token's pairs
+  for (int e = tid; e < p.E; e += kBlock) {
+    s_a[e] = 0;
+    s_b[e] = 0;
+  }
+  __syncthreads();
+  const int first_pos = t * p.k;
 #pragma unroll
-    for (int i = 0; i < kIdsPerThread; ++i) {
-      const int q = tid + i * kBlock;
-      if (i * kBlock < P) {  // uniform
-        const bool in = q < P;
-        const unsigned id = (unsigned)idv[i];
-        a += popc64(__ballot(in && id < ue));
-        bb += popc64(__ballot(in && id == ue && q < pos));
-        r += popc64(__ballot(in && id < urb));
+  for (int i = 0; i < kIdsPerThread; ++i) {
+    const int q = tid + i * kBlock;
+    if (q < P) {
+      const int e = idv[i];
+      if ((unsigned)e < (unsigned)p.E) {
+        atomicAdd(&s_a[e], 1);
+        if (q < first_pos) atomicAdd(&s_b[e], 1);
       }
-    }
-    if (lane_id() == 0) {
-      s_part[(w * kMaxTopK + j) * 3 + 0] = a;
-      s_part[(w * kMaxTopK + j) * 3 + 1] = bb;
-      s_part[(w * kMaxTopK + j) * 3 + 2] = r;
     }
   }
   __syncthreads();
+  // wave 0: exclusive prefix over 64 chunks of ceil(E/64) consecutive experts
+  const int csz = (p.E + kWave - 1) / kWave;
+  if (tid < kWave) {
+    int sum = 0;
+    const int lo = lane * csz, hi = min(lo + csz, p.E);
+    for (int e = lo; e < hi; ++e) sum += s_a[e];
+    s_chunk[lane] = wave_inclusive_sum(sum) - sum;
+  }
+  __syncthreads();
+  // slot j (wave 0, lane j): A = #valid ids below e, F = #valid ids below the
+  // first expert of e's rank, B = #ids == e before position t*k + j
   if (tid < p.k) {
-    const int j = tid;
-    int A = 0, B = 0, R = 0;
-    for (int w2 = 0; w2 < kWaves; ++w2) {
-      A += s_part[(w2 * kMaxTopK + j) * 3 + 0];
-      B += s_part[(w2 * kMaxTopK + j) * 3 + 1];
-      R += s_part[(w2 * kMaxTopK + j) * 3 + 2];
-    }
-    const int e = p.ids[t * p.k + j];
+    const int e = my_e;
     int row = -1;
     if ((unsigned)e < (unsigned)p.E) {
+      const int ci = e / csz;
+      int A = s_chunk[ci];
+      for (int x = ci * csz; x < e; ++x) A += s_a[x];
+      int B = s_b[e];
+      for (int j2 = 0; j2 < p.k; ++j2) {
+        const int o = __builtin_amdgcn_readlane(my_e, j2);
+        B += (j2 < lane && o == e) ? 1 : 0;
+      }
       if (p.C > 0) {
-        const int local = (A - R) + B;
+        const int first = (e / p.L) * p.L;
+        const int cf = first / csz;
+        int F = s_chunk[cf];
+        for (int x = cf * csz; x < first; ++x) F += s_a[x];
+        const int local = (A - F) + B;
         if (local < p.C) row = (e / p.L) * p.C + local;
       } else {
         row = A + B;
       }
     }
-    s_row[j] = row;
+    s_row[tid] = (row >= 0 && row < p.rows) ? row : -1;
   }
   __syncthreads();
   publish_rows(p, t, cc, s_row);
@@ -392,7 +415,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams
         row = p.expert_offsets[e] + pos;
       }
     }
-    s_row[threadIdx.x] = row;
+    s_row[threadIdx.x] = (row >= 0 && row < p.rows) ? row : -1;
   }
   __syncthreads();
   publish_rows(p, t, cc, s_row);
@@ -453,6 +476,7 @@ hipError_t launch_dispatch(const DispatchParams& in, hipStream_t st) {
   p.col_chunks = (nvec + vpc - 1) / vpc;
   const size_t P = (size_t)p.T * p.k;
   p.nchunks = (int)((P + kChunkPairs - 1) / kChunkPairs);
+  p.rows = p.C > 0 ? p.N * p.C : (int)P;
   if (P > (size_t)kSmallMaxPairs) {
     char* ws = reinterpret_cast<char*>(p.workspace);
     p.local_rank = reinterpret_cast<int32_t*>(ws);

@@ -30,6 +30,7 @@ struct DispatchParams {
   int32_t* chunk_hist;  // [nchunks][E] chunk histograms, then chunk bases
   int32_t* chunk_bad;   // [nchunks] chunk saw an id outside [0, E)
   int T, H, E, k, N, L, C;
+  int rows;  // receive rows addressed: N*C, or T*k when packed
   int payload;
   int nchunks;
   int col_chunks;     // blocks per token in the scatter

@@ -3,11 +3,15 @@
 // The router picks the experts each token goes to ("Enabling
 // trillion-parameter models on AWS EFA", Introduction) and hands the top-k
 // indices and scores to the dispatch ("Lower Latency and Higher Throughput
-// with Multi-Node DeepSeek Deployment", MoE Router).  Each lane holds
-// ceil(E/64) biased logits (coalesced: value i of lane l is expert i*64 + l);
-// k rounds of a 64-lane (value, index) arg-max pick the experts in descending
-// order, equal values going to the lower expert id.  Lanes 0..k-1 then form
-// the weights in fp32 and normalise them to sum to one.
+// with Multi-Node DeepSeek Deployment", MoE Router).
+//
+// Each lane holds ceil(E/64) biased logits (coalesced: value i of lane l is
+// expert i*64 + l) and sorts them once, best first, by (value descending, id
+// ascending).  Each of the k rounds then takes every lane's head, finds the
+// wave's best (value, id) with a DPP butterfly inside each 16-lane row and
+// four readlanes across the rows, and the owning lane pops its head.  Equal
+// values go to the lower expert id, so slots come out in descending order.
+// Lanes 0..k-1 then form the weights in fp32 and normalise them to one.
 #include "device_common.h"
 #include "launch.h"
 
@@ -16,15 +20,49 @@ namespace moe {
 namespace {
 
 constexpr int kRouteWaves = 4;  // tokens per 256-thread block
+constexpr int kNone = 0x7fffffff;
 
 __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 
+// One butterfly step: exchange with the lane given by a DPP pattern.
+template <int CTRL>
+__device__ __forceinline__ void dpp_max_step(float& v, int& i) {
+  const float ov =
+      __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+  const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xf, 0xf, false);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// Best (value, id) over the wave; the result is uniform.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  dpp_max_step<0xB1>(v, i);   // quad_perm [1,0,3,2]: lane ^ 1
+  dpp_max_step<0x4E>(v, i);   // quad_perm [2,3,0,1]: lane ^ 2
+  dpp_max_step<0x141>(v, i);  // row_half_mirror: quad <-> neighbouring quad
+  dpp_max_step<0x140>(v, i);  // row_mirror: half-row <-> other half-row
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+    const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+    if (better(rv, ri, bv, bi)) {
+      bv = rv;
+      bi = ri;
+    }
+  }
+  v = bv;
+  i = bi;
+}
+
 template <int VPL>
 __global__ void __launch_bounds__(kRouteWaves * kWave)
-route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
-                  int T, int E, int k, int score, int32_t* __restrict__ ids,
+route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bias, int T,
+                  int E, int k, int score, int32_t* __restrict__ ids,
                   float* __restrict__ weights) {
   const int lane = lane_id();
   const int t = blockIdx.x * kRouteWaves + (threadIdx.x / kWave);
@@ -32,6 +70,7 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
   const float* row = logits + (size_t)t * E;
 
   float v[VPL];
+  int id[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = i * kWave + lane;
@@ -39,38 +78,43 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
       float l = row[e];
       if (bias) l = l + bias[e];
       v[i] = l;
+      id[i] = e;
     } else {
       v[i] = -INFINITY;
+      id[i] = kNone;
     }
   }
-  uint32_t taken = 0;  // bit i: value i of this lane was chosen (or is padding)
+  // sort this lane's entries, best first (insertion network, fully unrolled)
 #pragma unroll
-  for (int i = 0; i < VPL; ++i)
-    if (i * kWave + lane >= E) taken |= 1u << i;
+  for (int a = 1; a < VPL; ++a) {
+#pragma unroll
+    for (int b = a; b > 0; --b) {
+      if (better(v[b], id[b], v[b - 1], id[b - 1])) {
+        const float tv = v[b];
+        v[b] = v[b - 1];
+        v[b - 1] = tv;
+        const int ti = id[b];
+        id[b] = id[b - 1];
+        id[b - 1] = ti;
+      }
+    }
+  }
 
-  float my_val = 0.0f;  // lane j keeps the biased logit of slot j
+  float my_val = 0.0f;  // lane j keeps the biased logit and id of slot j
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    float bv = v[0];
+    int bi = id[0];
+    wave_argmax(bv, bi);
+    if (bi == id[0]) {  // this lane owned the winner: pop its head
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e = i * kWave + lane;
-      if (!(taken & (1u << i)) && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
+      for (int i = 0; i + 1 < VPL; ++i) {
+        v[i] = v[i + 1];
+        id[i] = id[i + 1];
       }
+      v[VPL - 1] = -INFINITY;
+      id[VPL - 1] = kNone;
     }
-#pragma unroll
-    for (int d = kWave / 2; d > 0; d >>= 1) {
-      const float ov = __shfl_xor(bv, d, kWave);
-      const int oi = __shfl_xor(bi, d, kWave);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
     if (lane == j) {
       my_val = bv;
       my_id = bi;
