@@ -69,6 +69,19 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
+// Inclusive prefix sum over a wave64 with DPP: Hillis-Steele shifts inside
+// each 16-lane row (out-of-row sources read 0), then the row totals are
+// carried forward with the row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ int wave_inclusive_sum_dpp(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);

@@ -22,9 +22,9 @@
 //    histogram and scan and writes the metadata; every other block owns one
 //    (token, column chunk).  It loads the whole id list (a few ids per
 //    thread) and its slice of the token row at once, builds two LDS
-//    histograms (all ids; ids before this token), lets one wave scan 64 chunk
-//    sums of the first, reads its k rows off them, and stores its slice of
-//    the row k times.
+//    histograms (all ids; ids before this token); then each wave scans 64
+//    chunk sums of the first with DPP, reads its k rows off them into lanes
+//    0..k-1, and stores its slice of the row k times.
 //  * chunked (larger T*k): (1) per chunk of 1024 pairs, a block computes each
 //    pair's rank among equal experts inside the chunk (wave ballot matching,
 //    no atomics on the placement path) and the chunk's histogram; (2) one
@@ -96,7 +96,9 @@ __device__ void write_metadata(const DispatchParams& p, const int* cnt, const in
 }
 
 // ---------------------------------------------------------------------------
-// Scatter of one token's column slice to its k destination rows.
+// Scatter of one token's column slice to its k destination rows.  In every
+// wave, lane j < k holds the row of slot j (-1 = skipped); the store loop
+// reads it with readlane, so no LDS staging or barrier is needed.
 // ---------------------------------------------------------------------------
 template <int MAXV>
 __device__ __forceinline__ void load_slice(const DispatchParams& p, int t, int v0, int v1,
@@ -112,11 +114,11 @@ __device__ __forceinline__ void load_slice(const DispatchParams& p, int t, int v
 
 template <int MAXV>
 __device__ __forceinline__ void store_bf16(const DispatchParams& p, int v0, int v1,
-                                           const uint4 (&xv)[MAXV], const int* s_row) {
+                                           const uint4 (&xv)[MAXV], int row_lane) {
   const int nvec = p.H / 8;
   uint4* recv = reinterpret_cast<uint4*>(p.recv);
   for (int j = 0; j < p.k; ++j) {
-    const int row = s_row[j];
+    const int row = __builtin_amdgcn_readlane(row_lane, j);
     if (row < 0) continue;
     uint4* dst = recv + (size_t)row * nvec;
 #pragma unroll
@@ -131,12 +133,11 @@ __device__ __forceinline__ void store_bf16(const DispatchParams& p, int v0, int 
 // (v0 and v1 are multiples of 16, so a group is all in or all out).
 template <int MAXV>
 __device__ __forceinline__ void store_fp8(const DispatchParams& p, int v0, int v1,
-                                          const uint4 (&xv)[MAXV], const int* s_row) {
+                                          const uint4 (&xv)[MAXV], int row_lane) {
   const int nb = p.H / kFp8Block;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int v = v0 + threadIdx.x + i * kBlock;
-    if (v >= v1) continue;
     float f[8];
     const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
 #pragma unroll
@@ -149,6 +150,7 @@ __device__ __forceinline__ void store_fp8(const DispatchParams& p, int v0, int v
     for (int m = 0; m < 8; ++m) amax = fmaxf(amax, fabsf(f[m]));
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, kWave));
+    if (v >= v1) continue;
     const float s = amax / 448.0f;
     uint32_t lo = 0, hi = 0;
     if (amax != 0.0f) {
@@ -158,7 +160,7 @@ __device__ __forceinline__ void store_fp8(const DispatchParams& p, int v0, int v
       for (int m = 0; m < 4; ++m) hi |= f32_to_e4m3(f[4 + m] / s) << (8 * m);
     }
     for (int j = 0; j < p.k; ++j) {
-      const int row = s_row[j];
+      const int row = __builtin_amdgcn_readlane(row_lane, j);
       if (row < 0) continue;
       uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(p.recv) + (size_t)row * p.H);
       dst[v] = make_uint2(lo, hi);
@@ -167,14 +169,42 @@ __device__ __forceinline__ void store_fp8(const DispatchParams& p, int v0, int v
   }
 }
 
+// Block (t, cc == 0), wave 0, lanes j < k publish the rows of token t.
 __device__ __forceinline__ void publish_rows(const DispatchParams& p, int t, int cc,
-                                             const int* s_row) {
+                                             int row_lane) {
   if (cc == 0 && threadIdx.x < p.k) {
     const int q = t * p.k + threadIdx.x;
-    const int row = s_row[threadIdx.x];
-    p.token_row[q] = row;
-    if (p.row_src && row >= 0) p.row_src[row] = q;
+    p.token_row[q] = row_lane;
+    if (p.row_src && row_lane >= 0) p.row_src[row_lane] = q;
   }
+}
+
+// Experts per scan chunk: 64 chunks cover E; a power of two >= 4 so that a
+// chunk is read as whole 16-byte LDS vectors.
+__device__ __forceinline__ int chunk_size(int E) {
+  const int c = (E + kWave - 1) / kWave;
+  return c <= 4 ? 4 : (c <= 8 ? 8 : 16);
+}
+
+// Sum of the first `upto` entries of chunk `ci` (csz entries, 16-byte aligned).
+__device__ __forceinline__ int chunk_sum_below(const int* hist, int ci, int csz, int upto) {
+  const int4* c4 = reinterpret_cast<const int4*>(hist + ci * csz);
+  int4 q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = (4 * i < csz) ? c4[i] : make_int4(0, 0, 0, 0);
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s += (4 * i + 0 < upto) ? q[i].x : 0;
+    s += (4 * i + 1 < upto) ? q[i].y : 0;
+    s += (4 * i + 2 < upto) ? q[i].z : 0;
+    s += (4 * i + 3 < upto) ? q[i].w : 0;
+  }
+  return s;
+}
+
+__device__ __forceinline__ int checked_row(const DispatchParams& p, int row) {
+  return (row >= 0 && row < p.rows) ? row : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -182,11 +212,9 @@ __device__ __forceinline__ void publish_rows(const DispatchParams& p, int t, int
 // ---------------------------------------------------------------------------
 template <int PAYLOAD, int MAXV>
 __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p) {
-  __shared__ int s_a[kMaxExperts];      // histogram of all ids
+  __shared__ __align__(16) int s_a[kMaxExperts];  // histogram of all ids
   __shared__ int s_b[kMaxExperts + 1];  // block 0: scan; others: histogram before this token
   __shared__ int s_wave[kWaves];
-  __shared__ int s_chunk[kWave];        // exclusive prefix of 64 chunk sums of s_a
-  __shared__ int s_row[kMaxTopK];
   const int P = p.T * p.k;
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -239,7 +267,9 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   load_slice<MAXV>(p, t, v0, v1, xv);
 
   // two histograms: all ids, and ids at positions before this token's pairs
-  for (int e = tid; e < p.E; e += kBlock) {
+  // (s_a is cleared up to 64 whole chunks, so chunk reads see zeros past E)
+  const int csz = chunk_size(p.E);
+  for (int e = tid; e < kWave * csz; e += kBlock) {
     s_a[e] = 0;
     s_b[e] = 0;
   }
@@ -257,48 +287,43 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
     }
   }
   __syncthreads();
-  // wave 0: exclusive prefix over 64 chunks of ceil(E/64) consecutive experts
-  const int csz = (p.E + kWave - 1) / kWave;
-  if (tid < kWave) {
-    int sum = 0;
-    const int lo = lane * csz, hi = min(lo + csz, p.E);
-    for (int e = lo; e < hi; ++e) sum += s_a[e];
-    s_chunk[lane] = wave_inclusive_sum(sum) - sum;
-  }
-  __syncthreads();
-  // slot j (wave 0, lane j): A = #valid ids below e, F = #valid ids below the
-  // first expert of e's rank, B = #ids == e before position t*k + j
-  if (tid < p.k) {
-    const int e = my_e;
-    int row = -1;
-    if ((unsigned)e < (unsigned)p.E) {
-      const int ci = e / csz;
-      int A = s_chunk[ci];
-      for (int x = ci * csz; x < e; ++x) A += s_a[x];
-      int B = s_b[e];
-      for (int j2 = 0; j2 < p.k; ++j2) {
-        const int o = __builtin_amdgcn_readlane(my_e, j2);
-        B += (j2 < lane && o == e) ? 1 : 0;
-      }
-      if (p.C > 0) {
-        const int first = (e / p.L) * p.L;
-        const int cf = first / csz;
-        int F = s_chunk[cf];
-        for (int x = cf * csz; x < first; ++x) F += s_a[x];
-        const int local = (A - F) + B;
-        if (local < p.C) row = (e / p.L) * p.C + local;
-      } else {
-        row = A + B;
-      }
+
+  // Every wave on its own: lane l sums chunk l of csz consecutive experts, a
+  // DPP scan turns the chunk sums into exclusive chunk prefixes, and lane j
+  // reads off, for its slot's expert e:
+  //   A = #valid ids below e, F = #valid ids below the first expert of e's
+  //   rank, B = #ids == e at positions before t*k + j.
+  const bool valid = lane < p.k && (unsigned)my_e < (unsigned)p.E;
+  const int e = valid ? my_e : 0;
+  const int first = (e / p.L) * p.L;
+  // all LDS reads of this phase are independent and issued together
+  const int csum = chunk_sum_below(s_a, lane, csz, csz);
+  const int a_part = chunk_sum_below(s_a, e / csz, csz, e % csz);
+  const int f_part = chunk_sum_below(s_a, first / csz, csz, first % csz);
+  const int b_hist = s_b[e];
+  const int cexcl = wave_inclusive_sum_dpp(csum) - csum;
+  const int A = __shfl(cexcl, e / csz, kWave) + a_part;
+  const int F = __shfl(cexcl, first / csz, kWave) + f_part;
+  int row = -1;
+  if (valid) {
+    int B = b_hist;
+    for (int j2 = 0; j2 < p.k; ++j2) {
+      const int o = __builtin_amdgcn_readlane(my_e, j2);
+      B += (j2 < lane && o == e) ? 1 : 0;
     }
-    s_row[tid] = (row >= 0 && row < p.rows) ? row : -1;
+    if (p.C > 0) {
+      const int local = (A - F) + B;
+      if (local < p.C) row = (e / p.L) * p.C + local;
+    } else {
+      row = A + B;
+    }
   }
-  __syncthreads();
-  publish_rows(p, t, cc, s_row);
+  row = checked_row(p, row);
+  publish_rows(p, t, cc, row);
   if (PAYLOAD == 0)
-    store_bf16<MAXV>(p, v0, v1, xv, s_row);
+    store_bf16<MAXV>(p, v0, v1, xv, row);
   else
-    store_fp8<MAXV>(p, v0, v1, xv, s_row);
+    store_fp8<MAXV>(p, v0, v1, xv, row);
 }
 
 // ---------------------------------------------------------------------------
@@ -393,18 +418,18 @@ __global__ void __launch_bounds__(kBlock) layout_scan_kernel(DispatchParams p) {
 // Chunked path, kernel 3: rows from the chunk bases, then the scatter.
 template <int PAYLOAD, int MAXV>
 __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams p) {
-  __shared__ int s_row[kMaxTopK];
   const int t = blockIdx.x / p.col_chunks;
   const int cc = blockIdx.x - t * p.col_chunks;
   const int nvec = p.H / 8;
   const int v0 = cc * p.vec_per_chunk;
   const int v1 = min(v0 + p.vec_per_chunk, nvec);
+  const int lane = lane_id();
   uint4 xv[MAXV];
   load_slice<MAXV>(p, t, v0, v1, xv);
-  if (threadIdx.x < p.k) {
-    const int q = t * p.k + threadIdx.x;
+  int row = -1;
+  if (lane < p.k) {
+    const int q = t * p.k + lane;
     const int e = p.ids[q];
-    int row = -1;
     if ((unsigned)e < (unsigned)p.E) {
       const int pos = p.chunk_hist[(size_t)(q / kChunkPairs) * p.E + e] + p.local_rank[q];
       if (p.C > 0) {
@@ -415,14 +440,13 @@ __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams
         row = p.expert_offsets[e] + pos;
       }
     }
-    s_row[threadIdx.x] = (row >= 0 && row < p.rows) ? row : -1;
   }
-  __syncthreads();
-  publish_rows(p, t, cc, s_row);
+  row = checked_row(p, row);
+  publish_rows(p, t, cc, row);
   if (PAYLOAD == 0)
-    store_bf16<MAXV>(p, v0, v1, xv, s_row);
+    store_bf16<MAXV>(p, v0, v1, xv, row);
   else
-    store_fp8<MAXV>(p, v0, v1, xv, s_row);
+    store_fp8<MAXV>(p, v0, v1, xv, row);
 }
 
 template <int PAYLOAD, int MAXV>
