@@ -138,7 +138,7 @@ def run_gpu(args, w, inp):
                       else api.MOE_PAYLOAD_BF16)
     nbytes = algorithmic_bytes(w)
     per_step = nbytes["dispatch"] + nbytes["combine"] + nbytes["route"]
-    S = args.sets or max(2, math.ceil(2 * MALL_BYTES / per_step))
+    S = args.sets or min(64, max(2, math.ceil(2 * MALL_BYTES / per_step)))
     sets = [BufferSet(api, w, shape, inp, torch, np) for _ in range(S)]
     stream = torch.cuda.Stream()
 

@@ -1,6 +1,6 @@
 // capi.hip -- the C ABI of libmoe_dispatch.so: argument checks, then launches
 // on the caller's stream.  No allocation, no synchronisation, no state.
-#include "../../include/moe_dispatch.h"
+#include "moe_dispatch.h"
 #include "launch.h"
 
 namespace {

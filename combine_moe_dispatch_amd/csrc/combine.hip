@@ -7,9 +7,11 @@
 // chunk); the token's k rows and weights are read at uniform addresses (no
 // LDS staging, no barrier), each thread issues its k 16-byte gathers together
 // (8 at a time) and folds them with fp32 fused multiply-adds in slot order
-// from zero, then rounds to bf16 (nearest even) and stores 16 bytes.  With
-// the fp8 payload a thread owns 16 columns: one 16-byte gather of codes per row, each code decoded exactly to fp32 and multiplied by its
-// block's fp32 scale.  This is a bandwidth-bound gather-reduce: no MFMA.
+// from zero, then rounds to bf16 (nearest even) and stores 16 bytes.  The
+// gathers and the stores carry non-temporal (streaming) hints.  With
+// the fp8 payload a thread owns 16 columns: one 16-byte gather of codes per
+// row, each code decoded exactly to fp32 (the hardware OCP e4m3 convert) and
+// multiplied by its block's fp32 scale.  This is a bandwidth-bound gather-reduce: no MFMA.
 #include "device_common.h"
 #include "launch.h"
 
@@ -49,7 +51,7 @@ combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ tok
     uint4 yv[kGroup];
 #pragma unroll
     for (int g = 0; g < kGroup; ++g)
-      yv[g] = row[g] >= 0 ? y[(size_t)row[g] * nvec + v] : make_uint4(0, 0, 0, 0);
+      yv[g] = row[g] >= 0 ? load_stream(&y[(size_t)row[g] * nvec + v]) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
       if (row[g] < 0) continue;
@@ -66,7 +68,7 @@ combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ tok
   o.y = pack_bf16x2(acc[2], acc[3]);
   o.z = pack_bf16x2(acc[4], acc[5]);
   o.w = pack_bf16x2(acc[6], acc[7]);
-  out[(size_t)t * nvec + v] = o;
+  store_stream(&out[(size_t)t * nvec + v], o);
 }
 
 // fp8: vectors of 16 codes; 8 vectors share one 128-column scale.
@@ -97,25 +99,25 @@ combine_fp8_kernel(const uint4* __restrict__ y, const float* __restrict__ ys,
     float sc[kGroup];
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
-      yv[g] = row[g] >= 0 ? y[(size_t)row[g] * nvec + v] : make_uint4(0, 0, 0, 0);
-      sc[g] = row[g] >= 0 ? ys[(size_t)row[g] * nb + v / 8] : 0.0f;
+      yv[g] = row[g] >= 0 ? load_stream(&y[(size_t)row[g] * nvec + v]) : make_uint4(0, 0, 0, 0);
+      sc[g] = row[g] >= 0 ? load_stream(&ys[(size_t)row[g] * nb + v / 8]) : 0.0f;
     }
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
       if (row[g] < 0) continue;
       const uint32_t q[4] = {yv[g].x, yv[g].y, yv[g].z, yv[g].w};
+      float dec[16];
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const float val = e4m3_to_f32((q[m / 4] >> (8 * (m % 4))) & 0xffu) * sc[g];
-        acc[m] = fmaf(wj[g], val, acc[m]);
-      }
+      for (int m = 0; m < 4; ++m) e4m3x4_to_f32(q[m], dec + 4 * m);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) acc[m] = fmaf(wj[g], dec[m] * sc[g], acc[m]);
     }
   }
   uint4* o = out + (size_t)t * (H / 8) + 2 * (size_t)v;
-  o[0] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                    pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-  o[1] = make_uint4(pack_bf16x2(acc[8], acc[9]), pack_bf16x2(acc[10], acc[11]),
-                    pack_bf16x2(acc[12], acc[13]), pack_bf16x2(acc[14], acc[15]));
+  store_stream(&o[0], make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
+  store_stream(&o[1], make_uint4(pack_bf16x2(acc[8], acc[9]), pack_bf16x2(acc[10], acc[11]),
+                                 pack_bf16x2(acc[12], acc[13]), pack_bf16x2(acc[14], acc[15])));
 }
 
 }  // namespace

@@ -46,17 +46,43 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return sign | code;
 }
 
-// fp32 value of an e4m3fn code (exact).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  uint32_t s = (c & 0x80u) << 24;
-  uint32_t e = (c >> 3) & 15u;
-  uint32_t m = c & 7u;
-  if ((c & 0x7fu) == 0x7fu) return __uint_as_float(0x7fc00000u | s);
-  if (e == 0) return __uint_as_float(s | __float_as_uint((float)m * 0.001953125f));
-  return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+// fp32 values of the four e4m3fn codes packed in w (byte i -> f[i]), with the
+// gfx950 packed convert (OCP e4m3fn; exact, since every code is an fp32 value).
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* f) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Streaming (non-temporal) 16- and 8-byte global accesses, for data touched
+// once: the payload rows of dispatch and combine.  Measured on MI355X they
+// shorten both kernels (the caches need not hold or write back the stream).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
+  const u32x4 t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store_stream(uint2* p, uint2 v) {
+  const u32x2 t = {v.x, v.y};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ float load_stream(const float* p) {
+  return __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ void store_stream(float* p, float v) {
+  __builtin_nontemporal_store(v, p);
+}
 
 // Inclusive/exclusive sums over a wave64 with shuffles.
 __device__ __forceinline__ int wave_inclusive_sum(int v) {

@@ -31,7 +31,7 @@
 //    block turns the chunk histograms into per-chunk bases and the global
 //    metadata; (3) the scatter reads a pair's row from those.
 //
-// Rows move as 16-byte vectors; with the fp8 payload each group of 16 lanes
+// Rows move as 16-byte vectors with non-temporal (streaming) hints; with the fp8 payload each group of 16 lanes
 // owns one 128-column block, reduces its amax with in-group shuffles and
 // stores 8 codes per lane plus one scale per block and destination.
 #include "device_common.h"
@@ -108,7 +108,7 @@ __device__ __forceinline__ void load_slice(const DispatchParams& p, int t, int v
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int v = v0 + threadIdx.x + i * kBlock;
-    xv[i] = v < v1 ? x[v] : make_uint4(0, 0, 0, 0);
+    xv[i] = v < v1 ? load_stream(&x[v]) : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -124,7 +124,7 @@ __device__ __forceinline__ void store_bf16(const DispatchParams& p, int v0, int 
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
       const int v = v0 + threadIdx.x + i * kBlock;
-      if (v < v1) dst[v] = xv[i];
+      if (v < v1) store_stream(&dst[v], xv[i]);
     }
   }
 }
@@ -163,8 +163,8 @@ __device__ __forceinline__ void store_fp8(const DispatchParams& p, int v0, int v
       const int row = __builtin_amdgcn_readlane(row_lane, j);
       if (row < 0) continue;
       uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(p.recv) + (size_t)row * p.H);
-      dst[v] = make_uint2(lo, hi);
-      if ((threadIdx.x & 15) == 0) p.recv_scales[(size_t)row * nb + v / 16] = s;
+      store_stream(&dst[v], make_uint2(lo, hi));
+      if ((threadIdx.x & 15) == 0) store_stream(&p.recv_scales[(size_t)row * nb + v / 16], s);
     }
   }
 }
@@ -491,14 +491,19 @@ size_t dispatch_workspace_bytes(int T, int k, int E) {
 hipError_t launch_dispatch(const DispatchParams& in, hipStream_t st) {
   DispatchParams p = in;
   const int nvec = p.H / 8;
-  // column chunks of at most 256 vectors (one per thread), balanced, and a
-  // multiple of 16 vectors so an fp8 scale block never straddles two blocks
-  p.col_chunks = (nvec + kBlock - 1) / kBlock;
+  const size_t P = (size_t)p.T * p.k;
+  // Column chunks, balanced, a multiple of 16 vectors so an fp8 scale block
+  // never straddles two blocks.  One vector per thread, except where the
+  // fused path's per-block recount of all T*k ids is heavy (T*k > 2048):
+  // there two vectors per thread halve the number of recounting blocks
+  // (measured: fp8 at T*k = 4096, 16.6 -> 15.0 us; no gain below).
+  const bool wide = P > 2048 && P <= (size_t)kSmallMaxPairs;
+  const int budget = wide ? 2 * kBlock : kBlock;
+  p.col_chunks = (nvec + budget - 1) / budget;
   int vpc = (nvec + p.col_chunks - 1) / p.col_chunks;
   vpc = (vpc + 15) / 16 * 16;
   p.vec_per_chunk = vpc;
   p.col_chunks = (nvec + vpc - 1) / vpc;
-  const size_t P = (size_t)p.T * p.k;
   p.nchunks = (int)((P + kChunkPairs - 1) / kChunkPairs);
   p.rows = p.C > 0 ? p.N * p.C : (int)P;
   if (P > (size_t)kSmallMaxPairs) {

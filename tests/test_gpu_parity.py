@@ -68,6 +68,7 @@ SWEEP = [
     (513, 256, 256, 8, 32, 4104, 0, True, None),   # first chunked case
     (1000, 136, 8, 8, 2, 0, 0, False, 3),          # chunked, heavy duplicates
     (1000, 7168, 64, 1, 8, 0, 1, True, None),
+    (900, 1024, 32, 8, 4, 0, 1, False, 7),        # fp8, chunked path, duplicates
     (3000, 64, 1024, 8, 32, 0, 0, True, None),     # E at the library maximum
     (2048, 512, 256, 32, 256, 0, 0, True, None),   # k at the library maximum
 ]
@@ -179,3 +180,31 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {i}"
         assert (lay.token_row >= 0).all()
+
+
+def test_fp8_decode_all_codes_through_combine():
+    """All 256 e4m3 codes through moe_combine with k=1, weight 1 and scale 1.
+    Each finite code comes out as its exact value (e4m3 values are bf16 values),
+    except -0, which the fp32 chain fma(1, -0, +0) turns into +0 -- exactly as
+    the oracle's chain does; NaN codes come out as NaN."""
+    shape = api.Shape(1, 256, 1, 1, 1, 1, api.MOE_PAYLOAD_FP8_E4M3_B128)
+    codes = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    y = torch.from_numpy(codes).cuda()
+    ys = torch.ones(1, 2, dtype=torch.float32, device="cuda")
+    lay = api.Layout.empty(shape, "cuda")
+    lay.token_row.zero_()
+    w = torch.ones(1, 1, dtype=torch.float32, device="cuda")
+    out = torch.empty(1, 256, dtype=torch.int16, device="cuda")
+    api.moe_combine(shape, y, ys, lay, w, out)
+    torch.cuda.synchronize()
+    got = host_u16(out)[0]
+    ref = oracle.combine_f32_ordered(codes, np.ones((1, 2), np.float32),
+                                     np.zeros((1, 1), np.int32), np.ones((1, 1), np.float32))[0]
+    for c in range(256):
+        v = oracle.e4m3_to_f32(c)
+        if np.isnan(v):
+            assert (got[c] & 0x7F80) == 0x7F80 and (got[c] & 0x7F) != 0, c
+            continue
+        assert got[c] == ref[c], (c, hex(got[c]), hex(ref[c]))
+        if c != 0x80:
+            assert got[c] == oracle.f32_to_bf16(v), (c, hex(got[c]))
