@@ -64,6 +64,8 @@ def _load():
         lib.oracle_e4m3_to_f32.restype = f32
         lib.oracle_route_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
         lib.oracle_route_topk.restype = i32
+        lib.oracle_route_topk_grouped.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+        lib.oracle_route_topk_grouped.restype = i32
         lib.oracle_layout.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                       vp, vp, i64, vp]
         lib.oracle_layout.restype = i32
@@ -128,6 +130,23 @@ def route_topk(logits: np.ndarray, bias: Optional[np.ndarray], k: int, score: in
     rc = _load().oracle_route_topk(_ptr(logits), _ptr(b), T, E, k, score, _ptr(ids), _ptr(w))
     if rc != 0:
         raise ValueError("oracle_route_topk: invalid arguments or non-finite logits")
+    return ids, w
+
+
+def route_topk_grouped(logits: np.ndarray, bias: Optional[np.ndarray], k: int, score: int,
+                       n_groups: int, topk_groups: int):
+    """Group-limited top-k (DeepSeek-deployment page, MoE Router): keep the
+    topk_groups groups with the largest sum of their two best biased logits,
+    then the plain top-k over their experts."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    b = None if bias is None else _c(bias, np.float32)
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    rc = _load().oracle_route_topk_grouped(_ptr(logits), _ptr(b), T, E, k, score, n_groups,
+                                           topk_groups, _ptr(ids), _ptr(w))
+    if rc != 0:
+        raise ValueError("oracle_route_topk_grouped: invalid arguments or non-finite logits")
     return ids, w
 
 

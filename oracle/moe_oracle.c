@@ -140,6 +140,84 @@ int oracle_route_topk(const float *logits, const float *bias, int T, int E,
   return rc;
 }
 
+/* Group-limited routing (DeepSeek-deployment page, MoE Router: the same   */
+/* router serves every MoE model, plain top-k being the case where the top  */
+/* group set is all experts).  Steps, per token: biased logits; each group's */
+/* score = sum of its two largest biased logits (one fp32 add); keep the     */
+/* topk_groups best groups, ties to the lower group id; then the plain top-k */
+/* over the kept groups' experts and the same weights.                       */
+int oracle_route_topk_grouped(const float *logits, const float *bias, int T,
+                              int E, int k, int score, int n_groups,
+                              int topk_groups, int32_t *ids, float *weights) {
+  if (T < 0 || E < 1 || k < 1 || n_groups < 1 || E % n_groups != 0) return -1;
+  if (topk_groups < 1 || topk_groups > n_groups) return -1;
+  const int gsz = E / n_groups;
+  if (k > topk_groups * gsz) return -1;
+  if (score != ORACLE_SCORE_SOFTMAX && score != ORACLE_SCORE_SIGMOID) return -1;
+  float *lp = (float *)malloc(sizeof(float) * (size_t)E);
+  char *taken = (char *)malloc((size_t)E);
+  double *s = (double *)malloc(sizeof(double) * (size_t)k);
+  float *gscore = (float *)malloc(sizeof(float) * (size_t)n_groups);
+  char *keep = (char *)malloc((size_t)n_groups);
+  int rc = 0;
+  for (int t = 0; t < T && rc == 0; ++t) {
+    const float *row = logits + (size_t)t * E;
+    for (int g = 0; g < n_groups; ++g) {
+      /* the two largest biased logits of the group (first-seen on ties) */
+      int b1 = -1, b2 = -1;
+      float v1 = 0.0f, v2 = 0.0f;
+      for (int e = g * gsz; e < (g + 1) * gsz; ++e) {
+        float l = bias ? row[e] + bias[e] : row[e];
+        if (!isfinite(l)) rc = -1;
+        if (b1 < 0 || l > v1) {
+          b2 = b1;
+          v2 = v1;
+          b1 = e;
+          v1 = l;
+        } else if (b2 < 0 || l > v2) {
+          b2 = e;
+          v2 = l;
+        }
+      }
+      gscore[g] = (b2 < 0) ? v1 : v1 + v2;
+    }
+    if (rc) break;
+    memset(keep, 0, (size_t)n_groups);
+    for (int r = 0; r < topk_groups; ++r) {
+      int best = -1;
+      for (int g = 0; g < n_groups; ++g)
+        if (!keep[g] && (best < 0 || gscore[g] > gscore[best])) best = g;
+      keep[best] = 1;
+    }
+    /* the plain top-k over the experts of the kept groups */
+    for (int e = 0; e < E; ++e) lp[e] = bias ? row[e] + bias[e] : row[e];
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e)
+        if (keep[e / gsz] && !taken[e] && (best < 0 || lp[e] > lp[best])) best = e;
+      taken[best] = 1;
+      ids[(size_t)t * k + j] = best;
+    }
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) {
+      double l = (double)lp[ids[(size_t)t * k + j]];
+      if (score == ORACLE_SCORE_SIGMOID)
+        s[j] = 1.0 / (1.0 + exp(-l));
+      else
+        s[j] = exp(l - (double)lp[ids[(size_t)t * k]]);
+      sum += s[j];
+    }
+    for (int j = 0; j < k; ++j) weights[(size_t)t * k + j] = (float)(s[j] / sum);
+  }
+  free(lp);
+  free(taken);
+  free(s);
+  free(gscore);
+  free(keep);
+  return rc;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Layout (EFA page, Send and Receive Buffers and Dispatch and Combine:     */
 /* per-expert counts, their cumulative sum, offsets of contiguous regions). */

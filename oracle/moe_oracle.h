@@ -59,6 +59,16 @@ float oracle_e4m3_to_f32(uint8_t c);
 int oracle_route_topk(const float *logits, const float *bias, int T, int E,
                       int k, int score, int32_t *ids, float *weights);
 
+/* Group-limited top-k: experts form n_groups contiguous groups of E/n_groups;
+ * a group's score is the fp32 sum of its two largest biased logits (its only
+ * logit when a group has one expert); the topk_groups best groups are kept
+ * (ties to the lower group id) and the top-k is taken over their experts only,
+ * with the same ordering and weights as oracle_route_topk.  n_groups == 1
+ * reduces to oracle_route_topk.  Returns 0, or -1 on bad arguments. */
+int oracle_route_topk_grouped(const float *logits, const float *bias, int T,
+                              int E, int k, int score, int n_groups,
+                              int topk_groups, int32_t *ids, float *weights);
+
 /* Layout: counts, offsets and the destination row of every (token, slot)
  * pair.  C > 0: rank r owns rows [r*C, r*C + C); C == 0: packed regions.
  * row_src may be NULL; otherwise it has `rows` entries and only rows that
