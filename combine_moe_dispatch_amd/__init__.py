@@ -5,7 +5,7 @@ library ``libmoe_dispatch.so``); importing them loads the library and fails
 loudly when it has not been built.  ``inputs`` holds the seeded workload
 generators and does not need the library.
 """
-_API = ("moe_route_topk", "moe_dispatch", "moe_combine", "moe_expert_scale",
+_API = ("moe_route_topk", "moe_route_topk_grouped", "moe_dispatch", "moe_combine", "moe_expert_scale",
         "moe_recv_rows", "Shape", "Layout", "MoeError")
 
 

@@ -50,6 +50,8 @@ _lib.moe_dispatch_workspace_size.argtypes = [ctypes.POINTER(_Shape)]
 _lib.moe_dispatch_workspace_size.restype = ctypes.c_size_t
 _lib.moe_route_topk.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
 _lib.moe_route_topk.restype = _i32
+_lib.moe_route_topk_grouped.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+_lib.moe_route_topk_grouped.restype = _i32
 _lib.moe_dispatch.argtypes = [ctypes.POINTER(_Shape), _vp, _vp, _vp, _vp,
                               ctypes.POINTER(_Layout), _vp, ctypes.c_size_t, _vp]
 _lib.moe_dispatch.restype = _i32
@@ -153,6 +155,22 @@ def moe_route_topk(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int, s
         topk_weights = torch.empty(T, k, dtype=torch.float32, device=logits.device)
     _check(_lib.moe_route_topk(_ptr(logits), _ptr(bias), T, E, k, score, _ptr(topk_ids),
                                _ptr(topk_weights), _stream(stream)), "moe_route_topk")
+    return topk_ids, topk_weights
+
+
+def moe_route_topk_grouped(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int, score: int,
+                           n_groups: int, topk_groups: int,
+                           topk_ids: Optional[torch.Tensor] = None,
+                           topk_weights: Optional[torch.Tensor] = None, stream=None):
+    """Group-limited top-k routing; returns (topk_ids, topk_weights)."""
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    if topk_weights is None:
+        topk_weights = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _check(_lib.moe_route_topk_grouped(_ptr(logits), _ptr(bias), T, E, k, score, n_groups,
+                                       topk_groups, _ptr(topk_ids), _ptr(topk_weights),
+                                       _stream(stream)), "moe_route_topk_grouped")
     return topk_ids, topk_weights
 
 

@@ -64,8 +64,23 @@ moe_status moe_route_topk(const float* logits, const float* bias, int32_t T, int
   if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
   if (T > 0 && (!logits || !topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
   if ((int64_t)T * E > INT32_MAX * (int64_t)64) return MOE_ERR_UNSUPPORTED;
-  return from_hip(moe::launch_route_topk(logits, bias, T, E, k, score, topk_ids, topk_weights,
-                                         stream));
+  return from_hip(moe::launch_route_topk(logits, bias, T, E, k, score, 1, 1, topk_ids,
+                                         topk_weights, stream));
+}
+
+moe_status moe_route_topk_grouped(const float* logits, const float* bias, int32_t T, int32_t E,
+                                  int32_t k, int32_t score, int32_t n_groups,
+                                  int32_t topk_groups, int32_t* topk_ids, float* topk_weights,
+                                  hipStream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || n_groups < 1 || topk_groups < 1 || topk_groups > n_groups)
+    return MOE_ERR_INVALID_ARG;
+  if (E % n_groups != 0 || k > topk_groups * (E / n_groups)) return MOE_ERR_INVALID_ARG;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOP_K || n_groups > MOE_MAX_GROUPS)
+    return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!logits || !topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_route_topk(logits, bias, T, E, k, score, n_groups, topk_groups,
+                                         topk_ids, topk_weights, stream));
 }
 
 moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids,

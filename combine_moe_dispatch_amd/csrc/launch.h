@@ -41,7 +41,8 @@ size_t dispatch_workspace_bytes(int T, int k, int E);
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t st);
 
 hipError_t launch_route_topk(const float* logits, const float* bias, int T, int E, int k,
-                             int score, int32_t* ids, float* w, hipStream_t st);
+                             int score, int n_groups, int topk_groups, int32_t* ids, float* w,
+                             hipStream_t st);
 
 hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_row,
                           const float* w, void* out, int T, int H, int k, int payload,

@@ -12,6 +12,12 @@
 // four readlanes across the rows, and the owning lane pops its head.  Equal
 // values go to the lower expert id, so slots come out in descending order.
 // Lanes 0..k-1 then form the weights in fp32 and normalise them to one.
+//
+// Group-limited routing (same page, MoE Router: plain top-k is the case where
+// the kept groups are all experts): the wave stages its biased logits in LDS,
+// lane g sums the two largest logits of group g, topk_groups arg-max rounds
+// keep the best groups (ties to the lower group id), and the experts of the
+// other groups drop out before the top-k rounds.
 #include "device_common.h"
 #include "launch.h"
 
@@ -59,13 +65,22 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   i = bi;
 }
 
-template <int VPL>
+// LDS hand-off inside one wavefront (no block barrier: waves exit early).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int VPL, bool GROUPED>
 __global__ void __launch_bounds__(kRouteWaves * kWave)
 route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bias, int T,
-                  int E, int k, int score, int32_t* __restrict__ ids,
-                  float* __restrict__ weights) {
+                  int E, int k, int score, int n_groups, int topk_groups,
+                  int32_t* __restrict__ ids, float* __restrict__ weights) {
+  __shared__ float s_logit[GROUPED ? kRouteWaves : 1][GROUPED ? kMaxExperts : 1];
   const int lane = lane_id();
-  const int t = blockIdx.x * kRouteWaves + (threadIdx.x / kWave);
+  const int wave = threadIdx.x / kWave;
+  const int t = blockIdx.x * kRouteWaves + wave;
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
 
@@ -82,6 +97,50 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
     } else {
       v[i] = -INFINITY;
       id[i] = kNone;
+    }
+  }
+  if (GROUPED) {
+    float* sl = s_logit[wave];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (i * kWave + lane < E) sl[i * kWave + lane] = v[i];
+    wave_lds_sync();
+    // lane g: group score = sum of the group's two largest biased logits
+    const int gsz = E / n_groups;
+    float gv = -INFINITY;
+    int gi = kNone;
+    if (lane < n_groups) {
+      float m1 = -INFINITY, m2 = -INFINITY;
+      for (int e = lane * gsz; e < lane * gsz + gsz; ++e) {
+        const float l = sl[e];
+        if (l > m1) {
+          m2 = m1;
+          m1 = l;
+        } else if (l > m2) {
+          m2 = l;
+        }
+      }
+      gv = gsz > 1 ? m1 + m2 : m1;
+      gi = lane;
+    }
+    // keep the topk_groups best groups
+    uint64_t kept = 0;
+    for (int r = 0; r < topk_groups; ++r) {
+      float bv = gv;
+      int bi = gi;
+      wave_argmax(bv, bi);
+      kept |= 1ull << bi;
+      if (bi == gi) {
+        gv = -INFINITY;
+        gi = kNone;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      if (id[i] != kNone && !((kept >> (id[i] / gsz)) & 1ull)) {
+        v[i] = -INFINITY;
+        id[i] = kNone;
+      }
     }
   }
   // sort this lane's entries, best first (insertion network, fully unrolled)
@@ -138,25 +197,33 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
 
 template <int VPL>
 hipError_t launch_vpl(const float* logits, const float* bias, int T, int E, int k,
-                      int score, int32_t* ids, float* w, hipStream_t st) {
+                      int score, int n_groups, int topk_groups, int32_t* ids, float* w,
+                      hipStream_t st) {
   const int blocks = (T + kRouteWaves - 1) / kRouteWaves;
-  hipLaunchKernelGGL(route_topk_kernel<VPL>, dim3(blocks), dim3(kRouteWaves * kWave), 0, st,
-                     logits, bias, T, E, k, score, ids, w);
+  if (n_groups > 1 && topk_groups < n_groups)
+    hipLaunchKernelGGL((route_topk_kernel<VPL, true>), dim3(blocks), dim3(kRouteWaves * kWave),
+                       0, st, logits, bias, T, E, k, score, n_groups, topk_groups, ids, w);
+  else
+    hipLaunchKernelGGL((route_topk_kernel<VPL, false>), dim3(blocks), dim3(kRouteWaves * kWave),
+                       0, st, logits, bias, T, E, k, score, 1, 1, ids, w);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_route_topk(const float* logits, const float* bias, int T, int E, int k,
-                             int score, int32_t* ids, float* w, hipStream_t st) {
+                             int score, int n_groups, int topk_groups, int32_t* ids, float* w,
+                             hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int vpl = (E + kWave - 1) / kWave;
-  if (vpl <= 1) return launch_vpl<1>(logits, bias, T, E, k, score, ids, w, st);
-  if (vpl <= 2) return launch_vpl<2>(logits, bias, T, E, k, score, ids, w, st);
-  if (vpl <= 4) return launch_vpl<4>(logits, bias, T, E, k, score, ids, w, st);
-  if (vpl <= 6) return launch_vpl<6>(logits, bias, T, E, k, score, ids, w, st);
-  if (vpl <= 8) return launch_vpl<8>(logits, bias, T, E, k, score, ids, w, st);
-  return launch_vpl<16>(logits, bias, T, E, k, score, ids, w, st);
+#define MOE_ROUTE_ARGS logits, bias, T, E, k, score, n_groups, topk_groups, ids, w, st
+  if (vpl <= 1) return launch_vpl<1>(MOE_ROUTE_ARGS);
+  if (vpl <= 2) return launch_vpl<2>(MOE_ROUTE_ARGS);
+  if (vpl <= 4) return launch_vpl<4>(MOE_ROUTE_ARGS);
+  if (vpl <= 6) return launch_vpl<6>(MOE_ROUTE_ARGS);
+  if (vpl <= 8) return launch_vpl<8>(MOE_ROUTE_ARGS);
+  return launch_vpl<16>(MOE_ROUTE_ARGS);
+#undef MOE_ROUTE_ARGS
 }
 
 }  // namespace moe

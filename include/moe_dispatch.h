@@ -68,6 +68,7 @@ typedef enum {
 /* Limits of this library. */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 32
+#define MOE_MAX_GROUPS 64
 
 /* Sizes of one dispatch/combine problem (host struct, read during the call). */
 typedef struct {
@@ -124,6 +125,28 @@ moe_status moe_route_topk(const float *logits, const float *bias, int32_t T,
                           int32_t E, int32_t k, int32_t score,
                           int32_t *topk_ids, float *topk_weights,
                           hipStream_t stream);
+
+/*
+ * moe_route_topk_grouped -- group-limited top-k ([DSK] MoE Router: one router
+ * serves all MoE models; selecting among all experts is the special case in
+ * which every group is kept).
+ *
+ *   Experts form n_groups contiguous groups of E/n_groups.  A group's score
+ *   is the fp32 sum of its two largest biased logits (its only logit when a
+ *   group holds one expert).  The topk_groups groups with the largest scores
+ *   are kept (equal scores go to the lower group id); the top-k is then taken
+ *   over the kept groups' experts with the ordering and weights of
+ *   moe_route_topk.  n_groups == 1 or topk_groups == n_groups is exactly
+ *   moe_route_topk.
+ *   Other arguments as for moe_route_topk.
+ * Errors: MOE_ERR_INVALID_ARG unless E % n_groups == 0, 1 <= topk_groups <=
+ * n_groups and k <= topk_groups * (E / n_groups); MOE_ERR_UNSUPPORTED for
+ * n_groups > MOE_MAX_GROUPS.
+ */
+moe_status moe_route_topk_grouped(const float *logits, const float *bias, int32_t T,
+                                  int32_t E, int32_t k, int32_t score, int32_t n_groups,
+                                  int32_t topk_groups, int32_t *topk_ids,
+                                  float *topk_weights, hipStream_t stream);
 
 /*
  * moe_dispatch -- count, scan, place and scatter ([EFA] Send and Receive

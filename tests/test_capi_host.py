@@ -111,3 +111,12 @@ def test_route_rejects_bad_arguments():
 def test_status_strings():
     for code in range(4):
         assert api.moe_status_string(code).startswith("MOE_")
+
+
+def test_grouped_route_rejects_bad_arguments():
+    r = api._lib.moe_route_topk_grouped
+    assert r(16, None, 4, 16, 2, 1, 3, 1, 16, 16, None) == 1     # E % groups != 0
+    assert r(16, None, 4, 16, 2, 1, 4, 5, 16, 16, None) == 1     # topk_groups > groups
+    assert r(16, None, 4, 16, 2, 1, 4, 0, 16, 16, None) == 1     # topk_groups < 1
+    assert r(16, None, 4, 16, 9, 1, 4, 2, 16, 16, None) == 1     # k > kept experts
+    assert r(16, None, 4, 256, 2, 1, 128, 2, 16, 16, None) == 2  # too many groups

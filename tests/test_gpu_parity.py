@@ -208,3 +208,26 @@ def test_fp8_decode_all_codes_through_combine():
         assert got[c] == ref[c], (c, hex(got[c]), hex(ref[c]))
         if c != 0x80:
             assert got[c] == oracle.f32_to_bf16(v), (c, hex(got[c]))
+
+
+@pytest.mark.parametrize("T,E,G,TG,k,zipf,ties", [
+    (128, 256, 8, 4, 8, 0.0, False),   # DeepSeek-V3-style group routing
+    (4096, 256, 8, 4, 8, 1.2, False),  # with a popularity bias
+    (300, 384, 8, 2, 8, 0.0, True),    # many exact ties
+    (64, 64, 64, 5, 4, 0.0, False),    # one expert per group
+    (50, 256, 1, 1, 8, 0.0, False),    # one group: plain top-k
+])
+def test_grouped_route(T, E, G, TG, k, zipf, ties):
+    _announce(f"grouped route T={T} E={E} G={G} TG={TG} k={k}")
+    inp = inputs.generate(T, 8, E, 41 + E, zipf=zipf)
+    logits = inp.logits
+    if ties:
+        logits = np.random.default_rng(3).integers(-3, 4, size=(T, E)).astype(np.float32)
+    lg = torch.from_numpy(logits).cuda()
+    b = None if inp.bias is None else torch.from_numpy(inp.bias).cuda()
+    for score in (api.MOE_SCORE_SIGMOID, api.MOE_SCORE_SOFTMAX):
+        ids, w = api.moe_route_topk_grouped(lg, b, k, score, G, TG)
+        torch.cuda.synchronize()
+        o_ids, o_w = oracle.route_topk_grouped(logits, inp.bias, k, score, G, TG)
+        assert np.array_equal(ids.cpu().numpy(), o_ids)
+        np.testing.assert_allclose(w.cpu().numpy(), o_w, rtol=2.0 ** -20, atol=0)
