@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true")
+    ap.add_argument("--groups", type=int, default=1,
+                    help="route with group-limited top-k over this many expert groups")
+    ap.add_argument("--topk-groups", type=int, default=1, help="groups kept per token")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (PMC scale factor)")
     return ap.parse_args()
@@ -143,7 +146,11 @@ def run_gpu(args, w, inp):
     stream = torch.cuda.Stream()
 
     def route(s):
-        api.moe_route_topk(s.logits, s.bias, w.k, w.score, s.ids, s.w, stream=stream)
+        if args.groups > 1:
+            api.moe_route_topk_grouped(s.logits, s.bias, w.k, w.score, args.groups,
+                                       args.topk_groups, s.ids, s.w, stream=stream)
+        else:
+            api.moe_route_topk(s.logits, s.bias, w.k, w.score, s.ids, s.w, stream=stream)
 
     def dispatch(s):
         api.moe_dispatch(shape, s.x, s.ids, s.recv, s.rs, s.lay, s.ws, stream=stream)
@@ -310,6 +317,8 @@ def main():
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E,
                    "top_k": w.k, "ranks": w.N, "rank_capacity": w.C, "payload": w.payload,
                    "parallelism": "one source rank, N virtual destination ranks in HBM",
+                   "router": ("top-k" if args.groups <= 1 else
+                              f"group-limited top-k, {args.topk_groups} of {args.groups} groups"),
                    "cold_buffer_sets": g["sets"]},
         "dispatch_us": round(cold["dispatch_us"], 3),
         "combine_us": round(cold["combine_us"], 3),

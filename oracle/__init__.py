@@ -181,6 +181,40 @@ def layout(ids: np.ndarray, E: int, N: int, C: int, with_row_src: bool = True):
     return out
 
 
+def layout_sources(ids: np.ndarray, E: int, N: int, C: int):
+    """Every rank dispatching at once (EFA page, Send and Receive Buffers):
+    ids [S,T,k]; pairs placed in (rank, expert, source, token, slot) order.
+    Returns the layout dict plus source_counts [S,E] and source_offsets [E,S]."""
+    ids = _c(ids, np.int32)
+    S, T, k = ids.shape
+    rows = recv_rows(S * T, k, N, C)
+    out = {
+        "expert_counts": np.empty(E, np.int32),
+        "expert_offsets": np.empty(E, np.int32),
+        "rank_counts": np.empty(N, np.int32),
+        "rank_offsets": np.empty(N, np.int32),
+        "token_row": np.empty((S * T, k), np.int32),
+        "source_counts": np.empty((S, E), np.int32),
+        "source_offsets": np.empty((E, S), np.int32),
+    }
+    st = np.zeros(1, np.int32)
+    lib = _load()
+    lib.oracle_layout_sources.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int] + \
+                                         [ctypes.c_void_p] * 8
+    lib.oracle_layout_sources.restype = ctypes.c_int
+    rc = lib.oracle_layout_sources(_ptr(ids), S, T, k, E, N, C, _ptr(out["expert_counts"]),
+                                   _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]),
+                                   _ptr(out["rank_offsets"]), _ptr(out["token_row"]),
+                                   _ptr(out["source_counts"]), _ptr(out["source_offsets"]),
+                                   _ptr(st))
+    if rc != 0:
+        raise ValueError("oracle_layout_sources: invalid arguments")
+    out["status"] = int(st[0])
+    out["rows"] = rows
+    return out
+
+
 def dispatch_bf16(x_bits: np.ndarray, token_row: np.ndarray, rows: int,
                   fill: int = 0xFFFF) -> np.ndarray:
     """bf16 dispatch: every placed pair's row receives a copy of its token."""

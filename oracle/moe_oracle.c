@@ -303,6 +303,40 @@ int oracle_layout(const int32_t *ids, int T, int k, int E, int N, int C,
   return 0;
 }
 
+/* Every rank dispatching at once (EFA page, Send and Receive Buffers: the  */
+/* ranks first exchange their per-expert token counts, after which each     */
+/* knows where its writes go and at which offset it receives each rank's    */
+/* tokens).  Source s's tokens are global tokens s*T .. s*T+T-1, so sorting  */
+/* by (rank, expert, source, token, slot) is sorting the S*T tokens by       */
+/* (rank, expert, global token, slot): the single-source layout over all of  */
+/* them.  The exchanged count vectors and the per-source offsets follow.     */
+int oracle_layout_sources(const int32_t *ids, int S, int T, int k, int E, int N,
+                          int C, int32_t *expert_counts,
+                          int32_t *expert_offsets, int32_t *rank_counts,
+                          int32_t *rank_offsets, int32_t *token_row,
+                          int32_t *source_counts, int32_t *source_offsets,
+                          int32_t *status) {
+  if (S < 1 || T < 0 || (int64_t)S * T > INT32_MAX) return -1;
+  int rc = oracle_layout(ids, S * T, k, E, N, C, expert_counts, expert_offsets,
+                         rank_counts, rank_offsets, token_row, NULL, 0, status);
+  if (rc) return rc;
+  for (int s = 0; s < S; ++s) {
+    for (int e = 0; e < E; ++e) source_counts[(size_t)s * E + e] = 0;
+    for (size_t q = (size_t)s * T * k; q < (size_t)(s + 1) * T * k; ++q) {
+      int32_t e = ids[q];
+      if (e >= 0 && e < E) source_counts[(size_t)s * E + e] += 1;
+    }
+  }
+  for (int e = 0; e < E; ++e) {
+    int32_t run = expert_offsets[e];
+    for (int s = 0; s < S; ++s) {
+      source_offsets[(size_t)e * S + s] = run;
+      run += source_counts[(size_t)s * E + e];
+    }
+  }
+  return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Dispatch (EFA page, Introduction and MoE all-to-all over EFA: each token */
 /* goes to the ranks hosting its experts; Evaluation: block-scaled fp8      */

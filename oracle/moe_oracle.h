@@ -80,6 +80,19 @@ int oracle_layout(const int32_t *ids, int T, int k, int E, int N, int C,
                   int32_t *token_row, int32_t *row_src, int64_t rows,
                   int32_t *status);
 
+/* Multi-source layout: S sources each hold T tokens (ids [S][T][k]); the
+ * pairs of all sources are placed in (rank, expert, source, token, slot)
+ * order, with the same capacity rule as oracle_layout (C counts rows per rank
+ * across all sources).  token_row is [S*T*k].  Also writes source_counts
+ * [S][E] (pairs of source s routed to expert e) and source_offsets [E][S]
+ * (first row of source s's block inside expert e's segment). */
+int oracle_layout_sources(const int32_t *ids, int S, int T, int k, int E, int N,
+                          int C, int32_t *expert_counts,
+                          int32_t *expert_offsets, int32_t *rank_counts,
+                          int32_t *rank_offsets, int32_t *token_row,
+                          int32_t *source_counts, int32_t *source_offsets,
+                          int32_t *status);
+
 /* bf16 dispatch: recv[token_row[t*k+j]] = x[t] for every placed pair. */
 void oracle_dispatch_bf16(const uint16_t *x, int T, int H, int k,
                           const int32_t *token_row, uint16_t *recv);
