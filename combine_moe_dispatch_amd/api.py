@@ -183,6 +183,31 @@ def moe_dispatch(shape: Shape, x: torch.Tensor, topk_ids: torch.Tensor, recv_x: 
                              ws_bytes, _stream(stream)), "moe_dispatch")
 
 
+_lib.moe_dispatch_sources.argtypes = [ctypes.POINTER(_Shape), _i32, _vp, _vp, _vp, _vp,
+                                      ctypes.POINTER(_Layout), _vp, _vp, _vp, ctypes.c_size_t,
+                                      _vp]
+_lib.moe_dispatch_sources.restype = _i32
+
+
+def world_shape(shape: Shape, num_sources: int) -> Shape:
+    """The shape of all sources together (num_tokens = S*T)."""
+    return dataclasses.replace(shape, num_tokens=shape.num_tokens * num_sources)
+
+
+def moe_dispatch_sources(shape: Shape, num_sources: int, x: torch.Tensor,
+                         topk_ids: torch.Tensor, recv_x: torch.Tensor,
+                         recv_scales: Optional[torch.Tensor], layout: Layout,
+                         source_counts: torch.Tensor, source_offsets: torch.Tensor,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Every source rank dispatching at once; shape holds one source's sizes."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.moe_dispatch_sources(ctypes.byref(shape.c()), num_sources, _ptr(x),
+                                     _ptr(topk_ids), _ptr(recv_x), _ptr(recv_scales),
+                                     ctypes.byref(layout.c()), _ptr(source_counts),
+                                     _ptr(source_offsets), _ptr(workspace), ws_bytes,
+                                     _stream(stream)), "moe_dispatch_sources")
+
+
 def moe_expert_scale(shape: Shape, recv_x: torch.Tensor, recv_scales: Optional[torch.Tensor],
                      layout: Layout, alpha: torch.Tensor, y: torch.Tensor,
                      y_scales: Optional[torch.Tensor], stream=None) -> None:

@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmoe_dispatch.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["capi.hip", "route_topk.hip", "dispatch.hip", "combine.hip", "expert_scale.hip"]
+SOURCES = ["capi.hip", "route_topk.hip", "dispatch.hip", "sources.hip", "combine.hip",
+           "expert_scale.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -126,6 +126,30 @@ moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* to
   return from_hip(moe::launch_dispatch(p, stream));
 }
 
+moe_status moe_dispatch_sources(const moe_shape* shape, int32_t num_sources, const void* x,
+                                const int32_t* topk_ids, void* recv_x, float* recv_scales,
+                                const moe_layout* layout, int32_t* source_counts,
+                                int32_t* source_offsets, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (!shape || num_sources < 1) return MOE_ERR_INVALID_ARG;
+  const int64_t total = (int64_t)num_sources * shape->num_tokens;
+  if (total > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  moe_shape world = *shape;
+  world.num_tokens = (int32_t)total;
+  int L;
+  int64_t rows;
+  moe_status st = check_shape(&world, &L, &rows);
+  if (st != MOE_OK) return st;
+  if (!source_counts || !source_offsets) return MOE_ERR_INVALID_ARG;
+  st = moe_dispatch(&world, x, topk_ids, recv_x, recv_scales, layout, workspace, workspace_bytes,
+                    stream);
+  if (st != MOE_OK) return st;
+  return from_hip(moe::launch_source_metadata(topk_ids, num_sources, shape->num_tokens,
+                                              shape->top_k, shape->num_experts,
+                                              layout->expert_offsets, source_counts,
+                                              source_offsets, stream));
+}
+
 moe_status moe_expert_scale(const moe_shape* shape, const void* recv_x, const float* recv_scales,
                             const moe_layout* layout, const float* alpha, void* y,
                             float* y_scales, hipStream_t stream) {

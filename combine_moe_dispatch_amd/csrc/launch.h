@@ -44,6 +44,10 @@ hipError_t launch_route_topk(const float* logits, const float* bias, int T, int 
                              int score, int n_groups, int topk_groups, int32_t* ids, float* w,
                              hipStream_t st);
 
+hipError_t launch_source_metadata(const int32_t* ids, int S, int T, int k, int E,
+                                  const int32_t* expert_offsets, int32_t* source_counts,
+                                  int32_t* source_offsets, hipStream_t st);
+
 hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_row,
                           const float* w, void* out, int T, int H, int k, int payload,
                           hipStream_t st);

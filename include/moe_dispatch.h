@@ -181,6 +181,40 @@ moe_status moe_dispatch(const moe_shape *shape, const void *x,
                         hipStream_t stream);
 
 /*
+ * moe_dispatch_sources -- every rank of the expert-parallel world dispatching
+ * at once ([EFA] Send and Receive Buffers: ranks first exchange per-expert
+ * token counts, after which each knows where its writes go and at which
+ * offset it receives every rank's tokens).
+ *
+ *   shape         sizes of ONE source: num_tokens = T tokens per source; the
+ *                 rank capacity C (or packed regions, C == 0) covers the rows
+ *                 of all sources together.
+ *   num_sources   S >= 1 source ranks, all on this GPU.
+ *   x, topk_ids   [S][T][H] bf16 and [S][T][k] int32: source s's tokens are
+ *                 the global tokens s*T .. s*T+T-1.
+ *   recv_x, recv_scales, layout, workspace
+ *                 exactly as moe_dispatch for S*T tokens (size the receive
+ *                 buffer with moe_recv_rows and the workspace with
+ *                 moe_dispatch_workspace_size on num_tokens = S*T); inside
+ *                 each expert segment the pairs are in (source, token, slot)
+ *                 order; layout->token_row is [S*T*k].
+ *   source_counts [S][E] int32 out: pairs of source s routed to expert e (the
+ *                 count vectors the ranks exchange).
+ *   source_offsets [E][S] int32 out: first receive row of source s's block in
+ *                 expert e's segment (expert_offsets[e] plus the counts of the
+ *                 earlier sources); rows of pairs skipped for capacity are not
+ *                 written.
+ * The combine of the world is moe_combine with num_tokens = S*T.
+ * Errors as moe_dispatch; MOE_ERR_INVALID_ARG for S < 1 or null count arrays.
+ */
+moe_status moe_dispatch_sources(const moe_shape *shape, int32_t num_sources,
+                                const void *x, const int32_t *topk_ids, void *recv_x,
+                                float *recv_scales, const moe_layout *layout,
+                                int32_t *source_counts, int32_t *source_offsets,
+                                void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
  * moe_expert_scale -- stand-in for the experts' grouped GEMM between dispatch
  * and combine ([EFA] MoE all-to-all over EFA): every row of expert e's segment
  * is multiplied by alpha[e].  It reads the per-expert counts and offsets from

@@ -120,3 +120,14 @@ def test_grouped_route_rejects_bad_arguments():
     assert r(16, None, 4, 16, 2, 1, 4, 0, 16, 16, None) == 1     # topk_groups < 1
     assert r(16, None, 4, 16, 9, 1, 4, 2, 16, 16, None) == 1     # k > kept experts
     assert r(16, None, 4, 256, 2, 1, 128, 2, 16, 16, None) == 2  # too many groups
+
+
+def test_dispatch_sources_rejects_bad_arguments():
+    f = api._lib.moe_dispatch_sources
+    s = api._Shape(4, 64, 8, 2, 2, 0, 0)
+    lay = api._Layout(16, 16, 16, 16, 16, None, 16)
+    assert f(ctypes.byref(s), 0, 16, 16, 16, None, ctypes.byref(lay), 16, 16, None, 0, None) == 1
+    assert f(ctypes.byref(s), 2, 16, 16, 16, None, ctypes.byref(lay), None, 16, None, 0, None) == 1
+    assert f(None, 2, 16, 16, 16, None, ctypes.byref(lay), 16, 16, None, 0, None) == 1
+    bad = api._Shape(4, 64, 9, 2, 2, 0, 0)
+    assert f(ctypes.byref(bad), 2, 16, 16, 16, None, ctypes.byref(lay), 16, 16, None, 0, None) == 1

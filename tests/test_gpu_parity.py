@@ -231,3 +231,55 @@ def test_grouped_route(T, E, G, TG, k, zipf, ties):
         o_ids, o_w = oracle.route_topk_grouped(logits, inp.bias, k, score, G, TG)
         assert np.array_equal(ids.cpu().numpy(), o_ids)
         np.testing.assert_allclose(w.cpu().numpy(), o_w, rtol=2.0 ** -20, atol=0)
+
+
+@pytest.mark.parametrize("S,T,H,E,k,N,C,payload", [
+    (32, 128, 7168, 256, 8, 32, 0, 0),    # the whole DeepSeek-V3 EP32 decode world
+    (4, 50, 256, 24, 4, 4, 0, 0),
+    (3, 100, 256, 16, 4, 4, 160, 1),      # fixed capacity shared by all sources, overflow
+    (5, 0, 64, 8, 2, 2, 8, 0),            # no tokens
+])
+def test_dispatch_sources(S, T, H, E, k, N, C, payload):
+    """Every source rank dispatching at once: segments in (source, token, slot)
+    order, the exchanged per-source counts and per-source offsets, then the
+    world's combine."""
+    _announce(f"sources S={S} T={T} H={H} E={E} k={k} N={N} C={C} p={payload}")
+    inp = inputs.generate(S * T, H, E, 77 + S)
+    ids = np.stack([inputs.random_ids(T, k, E, 100 + s) for s in range(S)]) if T else \
+        np.zeros((S, 0, k), np.int32)
+    wts = inputs.random_weights(S * T, k, 5)
+    one = api.Shape(T, H, E, k, N, C, payload)
+    world = api.world_shape(one, S)
+    dev = "cuda"
+    x = dev_u16(inp.x_bits) if T else torch.empty(0, H, dtype=torch.int16, device=dev)
+    d_ids = torch.from_numpy(ids.reshape(S * T, k).copy()).to(dev)
+    lay = api.Layout.empty(world, dev)
+    recv, rs = api.alloc_recv(world, dev, fill=0x7F if payload else 0xFFFF)
+    ws = api.alloc_workspace(world, dev)
+    sc = torch.full((S, E), -9, dtype=torch.int32, device=dev)
+    so = torch.full((E, S), -9, dtype=torch.int32, device=dev)
+    api.moe_dispatch_sources(one, S, x, d_ids, recv, rs, lay, sc, so, ws)
+    torch.cuda.synchronize()
+    o = oracle.layout_sources(ids, E, N, C)
+    for key in ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "token_row",
+                "source_counts", "source_offsets"):
+        got = {"source_counts": sc, "source_offsets": so}.get(key)
+        got = getattr(lay, key) if got is None else got
+        assert np.array_equal(got.cpu().numpy().reshape(o[key].shape), o[key]), key
+    assert int(lay.status.item()) == o["status"]
+    if T == 0:
+        return
+    tr = o["token_row"]
+    if payload:
+        o_recv, o_rs = oracle.dispatch_fp8(inp.x_bits, tr, o["rows"], fill=0x7F)
+        assert np.array_equal(recv.cpu().numpy(), o_recv)
+        assert np.array_equal(rs.cpu().numpy().view(np.uint32), o_rs.view(np.uint32))
+    else:
+        o_recv = oracle.dispatch_bf16(inp.x_bits, tr, o["rows"], fill=0xFFFF)
+        assert np.array_equal(host_u16(recv), o_recv)
+    out = torch.empty(S * T, H, dtype=torch.int16, device=dev)
+    api.moe_combine(world, recv, rs, lay, torch.from_numpy(wts).to(dev), out)
+    torch.cuda.synchronize()
+    y = recv.cpu().numpy() if payload else host_u16(recv)
+    ys = rs.cpu().numpy() if payload else None
+    assert np.array_equal(host_u16(out), oracle.combine_f32_ordered(y, ys, tr, wts))
