@@ -61,7 +61,7 @@ def parse():
 # algorithmic bytes per launch (what the method must move)
 # ---------------------------------------------------------------------------
 def algorithmic_bytes(w):
-    T, H, E, k = w.T, w.H, w.E, w.k
+    T, H, E, k = w.tokens, w.H, w.E, w.k
     if w.payload == "fp8":
         row = H + 4 * (H // 128)
         dispatch = T * (2 * H + k * row + 8 * k)
@@ -120,13 +120,15 @@ class BufferSet:
         self.bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
         self.x = torch.from_numpy(inp.x_bits.view(np.int16).copy()).to(dev)
         self.alpha = torch.from_numpy(inp.alpha).to(dev)
-        self.ids = torch.empty(w.T, w.k, dtype=torch.int32, device=dev)
-        self.w = torch.empty(w.T, w.k, dtype=torch.float32, device=dev)
+        self.ids = torch.empty(w.tokens, w.k, dtype=torch.int32, device=dev)
+        self.w = torch.empty(w.tokens, w.k, dtype=torch.float32, device=dev)
+        self.src_counts = torch.empty(w.sources, w.E, dtype=torch.int32, device=dev)
+        self.src_offsets = torch.empty(w.E, w.sources, dtype=torch.int32, device=dev)
         self.lay = api.Layout.empty(shape, dev)
         self.ws = api.alloc_workspace(shape, dev)
         self.recv, self.rs = api.alloc_recv(shape, dev)
         self.y, self.ys = api.alloc_recv(shape, dev)
-        self.out = torch.empty(w.T, w.H, dtype=torch.int16, device=dev)
+        self.out = torch.empty(w.tokens, w.H, dtype=torch.int16, device=dev)
 
 
 def run_gpu(args, w, inp):
@@ -136,9 +138,10 @@ def run_gpu(args, w, inp):
     from combine_moe_dispatch_amd import api
 
     torch.cuda.set_device(0)
-    shape = api.Shape(w.T, w.H, w.E, w.k, w.N, w.C,
-                      api.MOE_PAYLOAD_FP8_E4M3_B128 if w.payload == "fp8"
-                      else api.MOE_PAYLOAD_BF16)
+    one = api.Shape(w.T, w.H, w.E, w.k, w.N, w.C,
+                    api.MOE_PAYLOAD_FP8_E4M3_B128 if w.payload == "fp8"
+                    else api.MOE_PAYLOAD_BF16)
+    shape = api.world_shape(one, w.sources)  # all sources' tokens together
     nbytes = algorithmic_bytes(w)
     per_step = nbytes["dispatch"] + nbytes["combine"] + nbytes["route"]
     S = args.sets or min(64, max(2, math.ceil(2 * MALL_BYTES / per_step)))
@@ -153,7 +156,11 @@ def run_gpu(args, w, inp):
             api.moe_route_topk(s.logits, s.bias, w.k, w.score, s.ids, s.w, stream=stream)
 
     def dispatch(s):
-        api.moe_dispatch(shape, s.x, s.ids, s.recv, s.rs, s.lay, s.ws, stream=stream)
+        if w.sources > 1:
+            api.moe_dispatch_sources(one, w.sources, s.x, s.ids, s.recv, s.rs, s.lay,
+                                     s.src_counts, s.src_offsets, s.ws, stream=stream)
+        else:
+            api.moe_dispatch(shape, s.x, s.ids, s.recv, s.rs, s.lay, s.ws, stream=stream)
 
     def combine(s):
         api.moe_combine(shape, s.y, s.ys, s.lay, s.w, s.out, stream=stream)
@@ -246,18 +253,19 @@ def cpu_baseline(w, inp, seconds):
     else:
         recv = np.zeros((rows, w.H), np.uint16)
         rs = None
-    out = np.empty((w.T, w.H), np.uint16)
+    T = w.tokens
+    out = np.empty((T, w.H), np.uint16)
     td = tc = 0.0
     reps = 0
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
         if fp8:
-            lib.oracle_dispatch_fp8(p(x), w.T, w.H, w.k, p(tr), p(recv), p(rs))
+            lib.oracle_dispatch_fp8(p(x), T, w.H, w.k, p(tr), p(recv), p(rs))
         else:
-            lib.oracle_dispatch_bf16(p(x), w.T, w.H, w.k, p(tr), p(recv))
+            lib.oracle_dispatch_bf16(p(x), T, w.H, w.k, p(tr), p(recv))
         t1 = time.perf_counter()
-        lib.oracle_combine_exact(p(recv), None if rs is None else p(rs), p(tr), p(wt), w.T,
+        lib.oracle_combine_exact(p(recv), None if rs is None else p(rs), p(tr), p(wt), T,
                                  w.k, w.H, p(out))
         t2 = time.perf_counter()
         td += t1 - t0
@@ -289,7 +297,7 @@ def main():
     from combine_moe_dispatch_amd import inputs
     w = inputs.WORKLOADS[args.workload]
     inp = inputs.generate_for(w)
-    print(f"[bench] workload {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} N={w.N} C={w.C} "
+    print(f"[bench] workload {w.name}: T={w.T} x {w.sources} source(s) H={w.H} E={w.E} k={w.k} N={w.N} C={w.C} "
           f"payload={w.payload}", file=sys.stderr, flush=True)
     g = run_gpu(args, w, inp)
     print(f"[bench] gpu timing done: {json.dumps(g)}", file=sys.stderr, flush=True)
@@ -314,7 +322,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.payload == "bf16" else "fp8-e4m3",
         "data": "synthetic (seeded N(0,1) logits and tokens of the workload's shape)",
-        "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E,
+        "config": {"workload": w.name, "tokens": w.T, "sources": w.sources,
+                   "hidden": w.H, "experts": w.E,
                    "top_k": w.k, "ranks": w.N, "rank_capacity": w.C, "payload": w.payload,
                    "parallelism": "one source rank, N virtual destination ranks in HBM",
                    "router": ("top-k" if args.groups <= 1 else

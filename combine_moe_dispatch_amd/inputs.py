@@ -37,14 +37,19 @@ class Workload:
     expert: str     # "identity" or "scale" (per-expert scalar stand-in)
     zipf: float     # 0 = no popularity bias, else the Zipf exponent
     seed: int
+    sources: int = 1  # source ranks dispatching at once (T tokens each)
 
     @property
     def L(self) -> int:
         return self.E // self.N
 
     @property
+    def tokens(self) -> int:
+        return self.T * self.sources
+
+    @property
     def rows(self) -> int:
-        return self.N * self.C if self.C > 0 else self.T * self.k
+        return self.N * self.C if self.C > 0 else self.tokens * self.k
 
 
 def _cap(T: int, k: int, E: int, N: int) -> int:
@@ -63,6 +68,10 @@ WORKLOADS = {
                                "bf16", "scale", 1.2, 1003),
     "fp8_payload": Workload("fp8_payload", 512, 7168, 256, 8, 32, _cap(512, 8, 256, 32),
                             SCORE_SIGMOID, "fp8", "scale", 0.0, 1004),
+    # all 32 ranks of a DeepSeek-V3 EP32 decode step dispatching at once
+    # (128 tokens each); packed receive regions sized by the exchanged counts
+    "dsv3_world": Workload("dsv3_world", 128, 7168, 256, 8, 32, 0, SCORE_SIGMOID, "bf16",
+                           "scale", 0.0, 1005, sources=32),
 }
 WORKLOAD_ORDER = ["tiny", "dsv3_decode", "kimi_k2_decode", "skewed_prefill", "fp8_payload"]
 
@@ -102,7 +111,7 @@ def generate(T: int, H: int, E: int, seed: int, expert: str = "scale",
 
 
 def generate_for(w: Workload) -> Inputs:
-    return generate(w.T, w.H, w.E, w.seed, w.expert, w.zipf)
+    return generate(w.tokens, w.H, w.E, w.seed, w.expert, w.zipf)
 
 
 def random_ids(T: int, k: int, E: int, seed: int, distinct: bool = True,

@@ -294,6 +294,48 @@ def _combine(fn, y, y_scales, token_row, weights):
     return out
 
 
+def combine_send(y, y_scales, token_row, ids, weights, E: int, N: int, exact: bool):
+    """Sender-side partial reduction, stage 1 (EFA page, Evaluation): one bf16
+    row per (token, distinct destination rank), ranks ascending.  Returns
+    (partial uint16 [T,M,H], partial_rank int32 [T,M]) with M = min(k, N);
+    rows of unused slots hold the poison 0xFFFF."""
+    tr = _c(token_row, np.int32)
+    ids = _c(ids, np.int32)
+    w = _c(weights, np.float32)
+    T, k = tr.shape
+    if y_scales is None:
+        y = _c(y, np.uint16)
+        ys = None
+    else:
+        y = _c(y, np.uint8)
+        ys = _c(y_scales, np.float32)
+    H = y.shape[1]
+    M = min(k, N)
+    partial = np.full((T, M, H), 0xFFFF, np.uint16)
+    prank = np.empty((T, M), np.int32)
+    lib = _load()
+    lib.oracle_combine_send.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + \
+        [ctypes.c_void_p] * 2
+    lib.oracle_combine_send.restype = None
+    lib.oracle_combine_send(_ptr(y), _ptr(ys), _ptr(tr), _ptr(ids), _ptr(w), T, k, H, E, N, M,
+                            1 if exact else 0, _ptr(partial), _ptr(prank))
+    return partial, prank
+
+
+def combine_recv(partial, partial_rank, exact: bool) -> np.ndarray:
+    """Stage 2: sum of each token's partial rows, in slot order, to bf16."""
+    partial = _c(partial, np.uint16)
+    prank = _c(partial_rank, np.int32)
+    T, M, H = partial.shape
+    out = np.empty((T, H), np.uint16)
+    lib = _load()
+    lib.oracle_combine_recv.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 4 + \
+        [ctypes.c_void_p]
+    lib.oracle_combine_recv.restype = None
+    lib.oracle_combine_recv(_ptr(partial), _ptr(prank), T, M, H, 1 if exact else 0, _ptr(out))
+    return out
+
+
 def combine_exact(y, y_scales, token_row, weights) -> np.ndarray:
     """Weighted sum of each token's returned rows in double precision, rounded
     once to bf16 (EFA page, Introduction; Evaluation)."""

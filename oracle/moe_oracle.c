@@ -473,3 +473,73 @@ void oracle_combine_f32_ordered(const void *y, const float *y_scales,
       out[(size_t)t * H + i] = oracle_f32_to_bf16(acc);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Sender-side partial reduction (EFA page, Evaluation: the alternative of   */
+/* accumulating on the sender reduces the data transferred, with possible    */
+/* precision implications).  Each destination rank first sums a token's      */
+/* rows for its own experts into one bf16 row per (token, rank); the origin  */
+/* then sums those rows.                                                     */
+/* ------------------------------------------------------------------------ */
+void oracle_combine_send(const void *y, const float *y_scales,
+                         const int32_t *token_row, const int32_t *ids,
+                         const float *w, int T, int k, int H, int E, int N,
+                         int M, int exact, uint16_t *partial,
+                         int32_t *partial_rank) {
+  const int L = E / N;
+  for (int t = 0; t < T; ++t) {
+    /* distinct ranks of the placed pairs, ascending */
+    int m = 0;
+    for (int r = 0; r < N; ++r) {
+      int hit = 0;
+      for (int j = 0; j < k; ++j) {
+        size_t p = (size_t)t * k + j;
+        if (token_row[p] >= 0 && ids[p] >= 0 && ids[p] < E && ids[p] / L == r) hit = 1;
+      }
+      if (hit) partial_rank[(size_t)t * M + m++] = r;
+    }
+    for (int i = m; i < M; ++i) partial_rank[(size_t)t * M + i] = -1;
+    for (int i = 0; i < m; ++i) {
+      const int r = partial_rank[(size_t)t * M + i];
+      uint16_t *dst = partial + ((size_t)t * M + i) * H;
+      for (int c = 0; c < H; ++c) {
+        double accd = 0.0;
+        float accf = 0.0f;
+        for (int j = 0; j < k; ++j) {
+          size_t p = (size_t)t * k + j;
+          int32_t row = token_row[p];
+          if (row < 0 || ids[p] < 0 || ids[p] >= E || ids[p] / L != r) continue;
+          if (exact) {
+            accd += (double)w[p] * oracle_payload_f64(y, y_scales, row, H, c);
+          } else {
+            float v;
+            if (!y_scales) {
+              v = oracle_bf16_to_f32(((const uint16_t *)y)[(size_t)row * H + c]);
+            } else {
+              uint8_t code = ((const uint8_t *)y)[(size_t)row * H + c];
+              v = oracle_e4m3_to_f32(code) * y_scales[(size_t)row * (H / 128) + c / 128];
+            }
+            accf = fmaf(w[p], v, accf);
+          }
+        }
+        dst[c] = exact ? oracle_f64_to_bf16(accd) : oracle_f32_to_bf16(accf);
+      }
+    }
+  }
+}
+
+void oracle_combine_recv(const uint16_t *partial, const int32_t *partial_rank,
+                         int T, int M, int H, int exact, uint16_t *out) {
+  for (int t = 0; t < T; ++t)
+    for (int c = 0; c < H; ++c) {
+      double accd = 0.0;
+      float accf = 0.0f;
+      for (int i = 0; i < M; ++i) {
+        if (partial_rank[(size_t)t * M + i] < 0) continue;
+        float v = oracle_bf16_to_f32(partial[((size_t)t * M + i) * H + c]);
+        accd += (double)v;
+        accf = accf + v;
+      }
+      out[(size_t)t * H + c] = exact ? oracle_f64_to_bf16(accd) : oracle_f32_to_bf16(accf);
+    }
+}

@@ -132,6 +132,24 @@ void oracle_combine_f32_ordered(const void *y, const float *y_scales,
                                 const int32_t *token_row, const float *w,
                                 int T, int k, int H, uint16_t *out);
 
+/* Sender-side partial reduction, stage 1: for token t, the distinct ranks of
+ * its placed pairs in ascending order r_0 < r_1 < ... get partial slots
+ * 0, 1, ... of M (M >= min(k, N)); slot i = bf16(sum over the pairs on rank
+ * r_i, in slot order, of w * v) and partial_rank[t][i] = r_i; unused slots
+ * get partial_rank -1 and their rows are left untouched.  exact != 0: the
+ * sum in double, one rounding; exact == 0: the fp32 fused multiply-add chain
+ * from 0.  partial is [T][M][H] bf16. */
+void oracle_combine_send(const void *y, const float *y_scales,
+                         const int32_t *token_row, const int32_t *ids,
+                         const float *w, int T, int k, int H, int E, int N,
+                         int M, int exact, uint16_t *partial,
+                         int32_t *partial_rank);
+
+/* Stage 2: out[t] = bf16(sum of the token's partial rows with rank >= 0, in
+ * slot order): double then one rounding (exact != 0) or fp32 adds from 0. */
+void oracle_combine_recv(const uint16_t *partial, const int32_t *partial_rank,
+                         int T, int M, int H, int exact, uint16_t *out);
+
 #ifdef __cplusplus
 }
 #endif
