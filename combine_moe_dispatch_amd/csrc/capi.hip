@@ -189,6 +189,43 @@ moe_status moe_combine(const moe_shape* shape, const void* expert_y, const float
                                       fp8 ? 1 : 0, stream));
 }
 
+moe_status moe_combine_send(const moe_shape* shape, const void* expert_y,
+                            const float* expert_scales, const moe_layout* layout,
+                            const int32_t* topk_ids, const float* topk_weights, void* partial,
+                            int32_t* partial_rank, hipStream_t stream) {
+  int L;
+  int64_t rows;
+  moe_status st = check_shape(shape, &L, &rows);
+  if (st != MOE_OK) return st;
+  const bool fp8 = shape->payload == MOE_PAYLOAD_FP8_E4M3_B128;
+  if (shape->num_tokens > 0) {
+    if (!layout || !layout->token_row || !expert_y || !topk_ids || !topk_weights || !partial ||
+        !partial_rank)
+      return MOE_ERR_INVALID_ARG;
+    if (!aligned16(expert_y) || !aligned16(partial)) return MOE_ERR_INVALID_ARG;
+    if (fp8 && !expert_scales) return MOE_ERR_INVALID_ARG;
+  }
+  return from_hip(moe::launch_combine_send(
+      expert_y, expert_scales, layout ? layout->token_row : nullptr, topk_ids, topk_weights,
+      partial, partial_rank, shape->num_tokens, shape->hidden, shape->top_k,
+      shape->num_experts, shape->num_ranks, fp8 ? 1 : 0, stream));
+}
+
+moe_status moe_combine_recv(const moe_shape* shape, const void* partial,
+                            const int32_t* partial_rank, void* out, hipStream_t stream) {
+  int L;
+  int64_t rows;
+  moe_status st = check_shape(shape, &L, &rows);
+  if (st != MOE_OK) return st;
+  if (shape->num_tokens > 0) {
+    if (!partial || !partial_rank || !out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(partial) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  }
+  const int M = shape->top_k < shape->num_ranks ? shape->top_k : shape->num_ranks;
+  return from_hip(moe::launch_combine_recv(partial, partial_rank, out, shape->num_tokens,
+                                           shape->hidden, M, stream));
+}
+
 const char* moe_status_string(moe_status status) {
   switch (status) {
     case MOE_OK: return "MOE_OK";

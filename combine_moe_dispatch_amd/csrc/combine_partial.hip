@@ -1,0 +1,215 @@
+// combine_partial.hip -- combine with sender-side partial reduction.
+//
+// The alternative to accumulating only on the receiving side: each
+// destination rank first sums a token's rows for its own experts and sends
+// one row per (token, rank), which transfers less data at some cost in
+// precision ("Enabling trillion-parameter models on AWS EFA", Evaluation).
+//
+// Stage 1 (send): for token t the distinct ranks of its placed pairs, in
+// ascending order, get partial slots 0..m-1 of M = min(k, N).  Slot i holds
+// bf16(fp32 fused multiply-add chain over the pairs on that rank, in slot
+// order from 0); partial_rank[t][i] names the rank, -1 marks an unused slot.
+// Stage 2 (recv): out[t] = bf16(fp32 sum of the used partial rows in slot
+// order from 0).
+//
+// A one-wave block owns (token, 64-vector column chunk).  Lane j holds slot
+// j's row, rank and weight; the rank grouping is a few readlanes; rows stream
+// in 8 at a time and are folded into up to GC group accumulators (more
+// groups take more passes).
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBlock = 64;  // one wavefront per block
+constexpr int kGroup = 8;   // row loads in flight per thread
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+template <bool FP8, int GC>
+__global__ void __launch_bounds__(kBlock)
+combine_send_kernel(const uint4* __restrict__ y, const float* __restrict__ ys,
+                    const int32_t* __restrict__ token_row, const int32_t* __restrict__ ids,
+                    const float* __restrict__ w, uint4* __restrict__ partial,
+                    int32_t* __restrict__ partial_rank, int H, int k, int E, int L, int M,
+                    int col_chunks) {
+  constexpr int kCols = FP8 ? 16 : 8;  // columns per thread
+  const int t = blockIdx.x / col_chunks;
+  const int cc = blockIdx.x - t * col_chunks;
+  const int nvec = H / kCols;
+  const int lane = threadIdx.x;
+  const int v = cc * kBlock + lane;
+  // lane j < k: slot j's row, rank (-1 if skipped) and weight
+  int my_row = -1, my_rank = -1;
+  float my_w = 0.0f;
+  if (lane < k) {
+    my_row = token_row[(size_t)t * k + lane];
+    const int e = ids[(size_t)t * k + lane];
+    my_rank = (my_row >= 0 && (unsigned)e < (unsigned)E) ? e / L : -1;
+    my_w = w[(size_t)t * k + lane];
+  }
+  // first slot of each rank, the number of distinct ranks, and each slot's
+  // group = the index of its rank among the distinct ranks in ascending order
+  bool first = my_rank >= 0;
+  for (int j = 0; j < k; ++j)
+    if (j < lane && __builtin_amdgcn_readlane(my_rank, j) == my_rank) first = false;
+  const uint64_t firsts = __ballot(first);
+  const int m = popc64(firsts);
+  int my_group = -1;
+  if (my_rank >= 0) {
+    my_group = 0;
+    for (int j = 0; j < k; ++j)
+      if (((firsts >> j) & 1ull) && __builtin_amdgcn_readlane(my_rank, j) < my_rank) ++my_group;
+  }
+  if (cc == 0 && lane < M) {
+    int r = -1;
+    for (int j = 0; j < k; ++j)
+      if (__builtin_amdgcn_readlane(my_group, j) == lane) r = __builtin_amdgcn_readlane(my_rank, j);
+    partial_rank[(size_t)t * M + lane] = r;
+  }
+  // lanes past the row end stay alive: later slots' values are read from
+  // every lane with readlane
+  const bool active = v < nvec;
+  const int nb = H / kFp8Block;
+  for (int g0 = 0; g0 < m; g0 += GC) {
+    float acc[GC][kCols];
+#pragma unroll
+    for (int q = 0; q < GC; ++q)
+#pragma unroll
+      for (int c = 0; c < kCols; ++c) acc[q][c] = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+      uint4 yv[kGroup];
+      float sc[kGroup];
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        const int j = j0 + g;
+        const int gj = j < k ? __builtin_amdgcn_readlane(my_group, j) : -1;
+        const int rj = j < k ? __builtin_amdgcn_readlane(my_row, j) : -1;
+        const bool use = active && gj >= g0 && gj < g0 + GC;
+        yv[g] = use ? load_stream(&y[(size_t)rj * nvec + v]) : make_uint4(0, 0, 0, 0);
+        sc[g] = (FP8 && use) ? load_stream(&ys[(size_t)rj * nb + v / 8]) : 0.0f;
+      }
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        const int j = j0 + g;
+        const int gj = j < k ? __builtin_amdgcn_readlane(my_group, j) : -1;
+        if (gj < g0 || gj >= g0 + GC) continue;
+        float val[kCols];
+        const uint32_t q4[4] = {yv[g].x, yv[g].y, yv[g].z, yv[g].w};
+        if (FP8) {
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) e4m3x4_to_f32(q4[c4], val + 4 * c4);
+#pragma unroll
+          for (int c = 0; c < kCols; ++c) val[c] = val[c] * sc[g];
+        } else {
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            val[2 * c4] = bf16_lo(q4[c4]);
+            val[2 * c4 + 1] = bf16_hi(q4[c4]);
+          }
+        }
+        const float wj = readlane_f(my_w, j);
+#pragma unroll
+        for (int q = 0; q < GC; ++q) {
+          if (gj != g0 + q) continue;
+#pragma unroll
+          for (int c = 0; c < kCols; ++c) acc[q][c] = fmaf(wj, val[c], acc[q][c]);
+        }
+      }
+    }
+    // partial rows are bf16: H / 8 vectors of 16 bytes each
+#pragma unroll
+    for (int q = 0; q < GC; ++q) {
+      if (!active || g0 + q >= m) continue;
+      uint4* dst = partial + ((size_t)t * M + g0 + q) * (H / 8) + (size_t)v * (kCols / 8);
+#pragma unroll
+      for (int h = 0; h < kCols / 8; ++h)
+        store_stream(&dst[h], make_uint4(pack_bf16x2(acc[q][8 * h + 0], acc[q][8 * h + 1]),
+                                         pack_bf16x2(acc[q][8 * h + 2], acc[q][8 * h + 3]),
+                                         pack_bf16x2(acc[q][8 * h + 4], acc[q][8 * h + 5]),
+                                         pack_bf16x2(acc[q][8 * h + 6], acc[q][8 * h + 7])));
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kBlock)
+combine_recv_kernel(const uint4* __restrict__ partial, const int32_t* __restrict__ partial_rank,
+                    uint4* __restrict__ out, int H, int M, int col_chunks) {
+  const int t = blockIdx.x / col_chunks;
+  const int cc = blockIdx.x - t * col_chunks;
+  const int nvec = H / 8;
+  const int v = cc * kBlock + threadIdx.x;
+  if (v >= nvec) return;
+  const int32_t* pr = partial_rank + (size_t)t * M;
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+  for (int i0 = 0; i0 < M; i0 += kGroup) {
+    uint4 pv[kGroup];
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      const int i = i0 + g;
+      pv[g] = (i < M && pr[i] >= 0) ? load_stream(&partial[((size_t)t * M + i) * nvec + v])
+                                    : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      const int i = i0 + g;
+      if (i >= M || pr[i] < 0) continue;
+      const uint32_t q4[4] = {pv[g].x, pv[g].y, pv[g].z, pv[g].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        acc[2 * m] = acc[2 * m] + bf16_lo(q4[m]);
+        acc[2 * m + 1] = acc[2 * m + 1] + bf16_hi(q4[m]);
+      }
+    }
+  }
+  store_stream(&out[(size_t)t * nvec + v],
+               make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                          pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
+}
+
+}  // namespace
+
+hipError_t launch_combine_send(const void* y, const float* ys, const int32_t* token_row,
+                               const int32_t* ids, const float* w, void* partial,
+                               int32_t* partial_rank, int T, int H, int k, int E, int N,
+                               int payload, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const int M = min(k, N);
+  const int nvec = payload == 0 ? H / 8 : H / 16;
+  const int col_chunks = (nvec + kBlock - 1) / kBlock;
+  const unsigned blocks = (unsigned)T * (unsigned)col_chunks;
+  if (payload == 0)
+    hipLaunchKernelGGL((combine_send_kernel<false, 8>), dim3(blocks), dim3(kBlock), 0, st,
+                       reinterpret_cast<const uint4*>(y), ys, token_row, ids, w,
+                       reinterpret_cast<uint4*>(partial), partial_rank, H, k, E, E / N, M,
+                       col_chunks);
+  else
+    hipLaunchKernelGGL((combine_send_kernel<true, 4>), dim3(blocks), dim3(kBlock), 0, st,
+                       reinterpret_cast<const uint4*>(y), ys, token_row, ids, w,
+                       reinterpret_cast<uint4*>(partial), partial_rank, H, k, E, E / N, M,
+                       col_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_recv(const void* partial, const int32_t* partial_rank, void* out,
+                               int T, int H, int M, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const int nvec = H / 8;
+  const int col_chunks = (nvec + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(combine_recv_kernel, dim3((unsigned)T * (unsigned)col_chunks), dim3(kBlock),
+                     0, st, reinterpret_cast<const uint4*>(partial), partial_rank,
+                     reinterpret_cast<uint4*>(out), H, M, col_chunks);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -52,6 +52,14 @@ hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_r
                           const float* w, void* out, int T, int H, int k, int payload,
                           hipStream_t st);
 
+hipError_t launch_combine_send(const void* y, const float* ys, const int32_t* token_row,
+                               const int32_t* ids, const float* w, void* partial,
+                               int32_t* partial_rank, int T, int H, int k, int E, int N,
+                               int payload, hipStream_t st);
+
+hipError_t launch_combine_recv(const void* partial, const int32_t* partial_rank, void* out,
+                               int T, int H, int M, hipStream_t st);
+
 hipError_t launch_expert_scale(const void* recv, const float* recv_scales,
                                const int32_t* expert_counts, const int32_t* expert_offsets,
                                const float* alpha, void* y, float* y_scales, int E, int L,

@@ -249,6 +249,31 @@ moe_status moe_combine(const moe_shape *shape, const void *expert_y,
                        const float *topk_weights, void *out,
                        hipStream_t stream);
 
+/*
+ * moe_combine_send / moe_combine_recv -- combine with sender-side partial
+ * reduction ([EFA] Evaluation: accumulating on the sender transfers less data,
+ * with possible precision implications; the pages' own kernels accumulate on
+ * the receiver only, which is moe_combine).
+ *
+ *   Let M = min(k, N).  For token t, the distinct ranks of its placed pairs
+ *   (token_row >= 0, valid id) in ascending order r_0 < r_1 < ... < r_{m-1}
+ *   own partial slots 0..m-1.
+ *   send: partial [T][M][H] bf16 -- slot i = bf16(fp32 fused multiply-add
+ *         chain over the pairs on rank r_i, in slot order, from 0; fp8 values
+ *         are fp32(code) * scale); partial_rank [T][M] int32 -- r_i, or -1
+ *         for slots i >= m, whose partial rows are not written.  Reads
+ *         layout->token_row, topk_ids [T][k] and topk_weights [T][k].
+ *   recv: out [T][H] bf16 = bf16(fp32 sum of the slots with partial_rank >= 0,
+ *         in slot order, from 0).
+ * With N == 1 the pair equals moe_combine.  Errors as moe_combine.
+ */
+moe_status moe_combine_send(const moe_shape *shape, const void *expert_y,
+                            const float *expert_scales, const moe_layout *layout,
+                            const int32_t *topk_ids, const float *topk_weights,
+                            void *partial, int32_t *partial_rank, hipStream_t stream);
+moe_status moe_combine_recv(const moe_shape *shape, const void *partial,
+                            const int32_t *partial_rank, void *out, hipStream_t stream);
+
 /* Static text for a status code.  Host function. */
 const char *moe_status_string(moe_status status);
 

@@ -131,3 +131,16 @@ def test_dispatch_sources_rejects_bad_arguments():
     assert f(None, 2, 16, 16, 16, None, ctypes.byref(lay), 16, 16, None, 0, None) == 1
     bad = api._Shape(4, 64, 9, 2, 2, 0, 0)
     assert f(ctypes.byref(bad), 2, 16, 16, 16, None, ctypes.byref(lay), 16, 16, None, 0, None) == 1
+
+
+def test_two_stage_combine_rejects_bad_arguments():
+    s = api._Shape(4, 64, 8, 2, 2, 0, 0)
+    lay = api._Layout(16, 16, 16, 16, 16, None, 16)
+    send, recv = api._lib.moe_combine_send, api._lib.moe_combine_recv
+    assert send(ctypes.byref(s), 16, None, ctypes.byref(lay), 16, 16, None, 16, None) == 1
+    assert send(ctypes.byref(s), 16, None, ctypes.byref(lay), None, 16, 16, 16, None) == 1
+    assert send(ctypes.byref(s), 16, None, ctypes.byref(lay), 16, 16, 8, 16, None) == 1
+    assert recv(ctypes.byref(s), 16, None, 16, None) == 1
+    assert recv(ctypes.byref(s), 16, 16, 24, None) == 1
+    bad = api._Shape(4, 64, 9, 2, 2, 0, 0)
+    assert recv(ctypes.byref(bad), 16, 16, 16, None) == 1
