@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--groups", type=int, default=1,
                     help="route with group-limited top-k over this many expert groups")
     ap.add_argument("--topk-groups", type=int, default=1, help="groups kept per token")
+    ap.add_argument("--combine", choices=("single", "two-stage"), default="single",
+                    help="receiver-only combine, or sender-side partial reduction + receive")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (PMC scale factor)")
     return ap.parse_args()
@@ -73,6 +75,11 @@ def algorithmic_bytes(w):
     return {"route": route, "dispatch": dispatch, "combine": combine}
 
 
+def nbytes_row(w):
+    """Bytes of one receive-buffer row (payload plus fp8 scales)."""
+    return w.H + 4 * (w.H // 128) if w.payload == "fp8" else 2 * w.H
+
+
 def source_sha():
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(ROOT, "combine_moe_dispatch_amd", "csrc", "*")))
@@ -82,10 +89,20 @@ def source_sha():
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload, kernel):
+def profile_tag(args):
+    """Name of the committed profile that matches these options."""
+    tag = args.workload
+    if args.combine == "two-stage":
+        tag += "_two_stage"
+    if args.groups > 1:
+        tag += "_grouped"
+    return tag
+
+
+def read_traffic(tag, kernel):
     """HBM bytes per launch from a committed PMC summary, if it was taken on
     the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -129,6 +146,9 @@ class BufferSet:
         self.recv, self.rs = api.alloc_recv(shape, dev)
         self.y, self.ys = api.alloc_recv(shape, dev)
         self.out = torch.empty(w.tokens, w.H, dtype=torch.int16, device=dev)
+        M = api.partial_slots(shape)
+        self.partial = torch.empty(w.tokens, M, w.H, dtype=torch.int16, device=dev)
+        self.prank = torch.empty(w.tokens, M, dtype=torch.int32, device=dev)
 
 
 def run_gpu(args, w, inp):
@@ -162,8 +182,21 @@ def run_gpu(args, w, inp):
         else:
             api.moe_dispatch(shape, s.x, s.ids, s.recv, s.rs, s.lay, s.ws, stream=stream)
 
+    two_stage = args.combine == "two-stage"
+
+    def combine_send(s):
+        api.moe_combine_send(shape, s.y, s.ys, s.lay, s.ids, s.w, s.partial, s.prank,
+                             stream=stream)
+
+    def combine_recv(s):
+        api.moe_combine_recv(shape, s.partial, s.prank, s.out, stream=stream)
+
     def combine(s):
-        api.moe_combine(shape, s.y, s.ys, s.lay, s.w, s.out, stream=stream)
+        if two_stage:
+            combine_send(s)
+            combine_recv(s)
+        else:
+            api.moe_combine(shape, s.y, s.ys, s.lay, s.w, s.out, stream=stream)
 
     def step(s):
         route(s)
@@ -178,6 +211,7 @@ def run_gpu(args, w, inp):
             combine(s)
     stream.synchronize()
     status = int(sets[0].lay.status.item())
+    partial_rows = int((sets[0].prank >= 0).sum().item()) if two_stage else 0
 
     def capture(fn_list, n, rotate):
         g = torch.cuda.CUDAGraph()
@@ -202,7 +236,7 @@ def run_gpu(args, w, inp):
         return e0.elapsed_time(e1) * 1e3 / n  # us per unit
 
     K, W = args.steps, args.warmup
-    res = {"sets": S, "status": status}
+    res = {"sets": S, "status": status, "partial_rows": partial_rows}
     for mode, rotate in (("cold", True), ("warm", False)):
         if mode == "warm" and args.no_warm:
             continue
@@ -226,6 +260,15 @@ def run_gpu(args, w, inp):
             "dispatch_us": time_graph(g_disp, K),
             "combine_us": time_graph(g_comb, K),
         }
+        if two_stage:
+            g_send = capture([combine_send], K, rotate)
+            g_recv = capture([combine_recv], K, rotate)
+            with torch.cuda.stream(stream):
+                g_send.replay()
+                g_recv.replay()
+            r["combine_send_us"] = time_graph(g_send, K)
+            r["combine_recv_us"] = time_graph(g_recv, K)
+            del g_send, g_recv
         res[mode] = r
         del g_step, g_route, g_disp, g_comb
     return res
@@ -302,6 +345,15 @@ def main():
     g = run_gpu(args, w, inp)
     print(f"[bench] gpu timing done: {json.dumps(g)}", file=sys.stderr, flush=True)
     nbytes = algorithmic_bytes(w)
+    if args.combine == "two-stage":
+        # send: the k rows and (row, id, weight) per pair in, one bf16 row per
+        # used (token, rank) slot and the slot ranks out; recv: those back in,
+        # the token out
+        M = min(w.k, w.N)
+        send = w.tokens * (nbytes_row(w) * w.k + 12 * w.k + 4 * M) + g["partial_rows"] * 2 * w.H
+        recv = g["partial_rows"] * 2 * w.H + w.tokens * (4 * M + 2 * w.H)
+        nbytes["combine"] = send + recv
+        nbytes["combine_send"], nbytes["combine_recv"] = send, recv
     cold = g["cold"]
     dc_us = cold["dispatch_us"] + cold["combine_us"]
     dc_bytes = nbytes["dispatch"] + nbytes["combine"]
@@ -326,6 +378,8 @@ def main():
                    "hidden": w.H, "experts": w.E,
                    "top_k": w.k, "ranks": w.N, "rank_capacity": w.C, "payload": w.payload,
                    "parallelism": "one source rank, N virtual destination ranks in HBM",
+                   "combine": ("receiver-only" if args.combine == "single" else
+                               "sender-side partial reduction, then receive"),
                    "router": ("top-k" if args.groups <= 1 else
                               f"group-limited top-k, {args.topk_groups} of {args.groups} groups"),
                    "cold_buffer_sets": g["sets"]},
@@ -339,9 +393,13 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": read_traffic(w.name, dom)},
+                     "traffic": read_traffic(profile_tag(args), dom)},
         "device_status": g["status"],
     }
+    if "combine_send_us" in cold:
+        line["two_stage_combine"] = {
+            "send_us": round(cold["combine_send_us"], 3), "recv_us": round(cold["combine_recv_us"], 3),
+            "partial_rows": g["partial_rows"], "rows_per_token": round(g["partial_rows"] / w.tokens, 3)}
     if "warm" in g:
         wm = g["warm"]
         wus = wm["dispatch_us"] + wm["combine_us"]
