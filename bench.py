@@ -131,7 +131,7 @@ def copy_calibration():
 
 
 class BufferSet:
-    def __init__(self, api, w, shape, inp, torch, np):
+    def __init__(self, api, w, shape, inp, torch, np, two_stage=False):
         dev = "cuda"
         self.logits = torch.from_numpy(inp.logits).to(dev)
         self.bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
@@ -146,7 +146,7 @@ class BufferSet:
         self.recv, self.rs = api.alloc_recv(shape, dev)
         self.y, self.ys = api.alloc_recv(shape, dev)
         self.out = torch.empty(w.tokens, w.H, dtype=torch.int16, device=dev)
-        M = api.partial_slots(shape)
+        M = api.partial_slots(shape) if two_stage else 0
         self.partial = torch.empty(w.tokens, M, w.H, dtype=torch.int16, device=dev)
         self.prank = torch.empty(w.tokens, M, dtype=torch.int32, device=dev)
 
@@ -165,7 +165,8 @@ def run_gpu(args, w, inp):
     nbytes = algorithmic_bytes(w)
     per_step = nbytes["dispatch"] + nbytes["combine"] + nbytes["route"]
     S = args.sets or min(64, max(2, math.ceil(2 * MALL_BYTES / per_step)))
-    sets = [BufferSet(api, w, shape, inp, torch, np) for _ in range(S)]
+    sets = [BufferSet(api, w, shape, inp, torch, np, args.combine == "two-stage")
+            for _ in range(S)]
     stream = torch.cuda.Stream()
 
     def route(s):
@@ -185,11 +186,11 @@ def run_gpu(args, w, inp):
     two_stage = args.combine == "two-stage"
 
     def combine_send(s):
-        api.moe_combine_send(shape, s.y, s.ys, s.lay, s.ids, s.w, s.partial, s.prank,
+        api.moe_combine_partial_send(shape, s.y, s.ys, s.lay, s.ids, s.w, s.partial, s.prank,
                              stream=stream)
 
     def combine_recv(s):
-        api.moe_combine_recv(shape, s.partial, s.prank, s.out, stream=stream)
+        api.moe_combine_partial_recv(shape, s.partial, s.prank, s.out, stream=stream)
 
     def combine(s):
         if two_stage:

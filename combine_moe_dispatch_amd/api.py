@@ -224,11 +224,11 @@ def moe_combine(shape: Shape, expert_y: torch.Tensor, expert_scales: Optional[to
                             _stream(stream)), "moe_combine")
 
 
-_lib.moe_combine_send.argtypes = [ctypes.POINTER(_Shape), _vp, _vp, ctypes.POINTER(_Layout),
+_lib.moe_combine_partial_send.argtypes = [ctypes.POINTER(_Shape), _vp, _vp, ctypes.POINTER(_Layout),
                                   _vp, _vp, _vp, _vp, _vp]
-_lib.moe_combine_send.restype = _i32
-_lib.moe_combine_recv.argtypes = [ctypes.POINTER(_Shape), _vp, _vp, _vp, _vp]
-_lib.moe_combine_recv.restype = _i32
+_lib.moe_combine_partial_send.restype = _i32
+_lib.moe_combine_partial_recv.argtypes = [ctypes.POINTER(_Shape), _vp, _vp, _vp, _vp]
+_lib.moe_combine_partial_recv.restype = _i32
 
 
 def partial_slots(shape: Shape) -> int:
@@ -236,21 +236,21 @@ def partial_slots(shape: Shape) -> int:
     return min(shape.top_k, shape.num_ranks)
 
 
-def moe_combine_send(shape: Shape, expert_y: torch.Tensor, expert_scales: Optional[torch.Tensor],
+def moe_combine_partial_send(shape: Shape, expert_y: torch.Tensor, expert_scales: Optional[torch.Tensor],
                      layout: Layout, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
                      partial: torch.Tensor, partial_rank: torch.Tensor, stream=None) -> None:
     """Stage 1 of the two-stage combine: one bf16 row per (token, rank)."""
-    _check(_lib.moe_combine_send(ctypes.byref(shape.c()), _ptr(expert_y), _ptr(expert_scales),
+    _check(_lib.moe_combine_partial_send(ctypes.byref(shape.c()), _ptr(expert_y), _ptr(expert_scales),
                                  ctypes.byref(layout.c()), _ptr(topk_ids), _ptr(topk_weights),
                                  _ptr(partial), _ptr(partial_rank), _stream(stream)),
-           "moe_combine_send")
+           "moe_combine_partial_send")
 
 
-def moe_combine_recv(shape: Shape, partial: torch.Tensor, partial_rank: torch.Tensor,
+def moe_combine_partial_recv(shape: Shape, partial: torch.Tensor, partial_rank: torch.Tensor,
                      out: torch.Tensor, stream=None) -> None:
     """Stage 2: sum of each token's partial rows."""
-    _check(_lib.moe_combine_recv(ctypes.byref(shape.c()), _ptr(partial), _ptr(partial_rank),
-                                 _ptr(out), _stream(stream)), "moe_combine_recv")
+    _check(_lib.moe_combine_partial_recv(ctypes.byref(shape.c()), _ptr(partial), _ptr(partial_rank),
+                                 _ptr(out), _stream(stream)), "moe_combine_partial_recv")
 
 
 def moe_status_string(status: int) -> str:

@@ -189,7 +189,7 @@ moe_status moe_combine(const moe_shape* shape, const void* expert_y, const float
                                       fp8 ? 1 : 0, stream));
 }
 
-moe_status moe_combine_send(const moe_shape* shape, const void* expert_y,
+moe_status moe_combine_partial_send(const moe_shape* shape, const void* expert_y,
                             const float* expert_scales, const moe_layout* layout,
                             const int32_t* topk_ids, const float* topk_weights, void* partial,
                             int32_t* partial_rank, hipStream_t stream) {
@@ -211,7 +211,7 @@ moe_status moe_combine_send(const moe_shape* shape, const void* expert_y,
       shape->num_experts, shape->num_ranks, fp8 ? 1 : 0, stream));
 }
 
-moe_status moe_combine_recv(const moe_shape* shape, const void* partial,
+moe_status moe_combine_partial_recv(const moe_shape* shape, const void* partial,
                             const int32_t* partial_rank, void* out, hipStream_t stream) {
   int L;
   int64_t rows;

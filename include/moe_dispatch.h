@@ -250,7 +250,7 @@ moe_status moe_combine(const moe_shape *shape, const void *expert_y,
                        hipStream_t stream);
 
 /*
- * moe_combine_send / moe_combine_recv -- combine with sender-side partial
+ * moe_combine_partial_send / moe_combine_partial_recv -- combine with sender-side partial
  * reduction ([EFA] Evaluation: accumulating on the sender transfers less data,
  * with possible precision implications; the pages' own kernels accumulate on
  * the receiver only, which is moe_combine).
@@ -267,11 +267,11 @@ moe_status moe_combine(const moe_shape *shape, const void *expert_y,
  *         in slot order, from 0).
  * With N == 1 the pair equals moe_combine.  Errors as moe_combine.
  */
-moe_status moe_combine_send(const moe_shape *shape, const void *expert_y,
+moe_status moe_combine_partial_send(const moe_shape *shape, const void *expert_y,
                             const float *expert_scales, const moe_layout *layout,
                             const int32_t *topk_ids, const float *topk_weights,
                             void *partial, int32_t *partial_rank, hipStream_t stream);
-moe_status moe_combine_recv(const moe_shape *shape, const void *partial,
+moe_status moe_combine_partial_recv(const moe_shape *shape, const void *partial,
                             const int32_t *partial_rank, void *out, hipStream_t stream);
 
 /* Static text for a status code.  Host function. */

@@ -136,7 +136,7 @@ def test_dispatch_sources_rejects_bad_arguments():
 def test_two_stage_combine_rejects_bad_arguments():
     s = api._Shape(4, 64, 8, 2, 2, 0, 0)
     lay = api._Layout(16, 16, 16, 16, 16, None, 16)
-    send, recv = api._lib.moe_combine_send, api._lib.moe_combine_recv
+    send, recv = api._lib.moe_combine_partial_send, api._lib.moe_combine_partial_recv
     assert send(ctypes.byref(s), 16, None, ctypes.byref(lay), 16, 16, None, 16, None) == 1
     assert send(ctypes.byref(s), 16, None, ctypes.byref(lay), None, 16, 16, 16, None) == 1
     assert send(ctypes.byref(s), 16, None, ctypes.byref(lay), 16, 16, 8, 16, None) == 1

@@ -1,6 +1,6 @@
 """GPU parity of the two-stage combine (sender-side partial reduction).
 
-Stage 1 (moe_combine_send) and stage 2 (moe_combine_recv) through the C ABI
+Stage 1 (moe_combine_partial_send) and stage 2 (moe_combine_partial_recv) through the C ABI
 against the oracle fed the GPU's own inputs to each stage: bit-exact against
 the fp32-chain forms, within 1 bf16 ulp of the double-precision forms; unused
 partial rows stay poisoned.  The result's distance from the single-stage
@@ -46,9 +46,9 @@ def test_two_stage_combine(T, H, E, k, N, C, payload, skew):
     api.moe_expert_scale(shape, recv, rs, lay, torch.from_numpy(inp.alpha).to(dev), y, ys)
     partial = torch.full((T, M, H), -1, dtype=torch.int16, device=dev)   # 0xFFFF poison
     prank = torch.full((T, M), -7, dtype=torch.int32, device=dev)
-    api.moe_combine_send(shape, y, ys, lay, d_ids, d_w, partial, prank)
+    api.moe_combine_partial_send(shape, y, ys, lay, d_ids, d_w, partial, prank)
     out = torch.empty(T, H, dtype=torch.int16, device=dev)
-    api.moe_combine_recv(shape, partial, prank, out)
+    api.moe_combine_partial_recv(shape, partial, prank, out)
     torch.cuda.synchronize()
     if T == 0:
         return
