@@ -253,6 +253,32 @@ def moe_combine_partial_recv(shape: Shape, partial: torch.Tensor, partial_rank: 
                                  _ptr(out), _stream(stream)), "moe_combine_partial_recv")
 
 
+_lib.moe_dispatch_recv.argtypes = [ctypes.POINTER(_Shape), _vp, _vp, ctypes.POINTER(_Layout),
+                                   _vp, _vp, _vp, _vp]
+_lib.moe_dispatch_recv.restype = _i32
+_lib.moe_combine_send.argtypes = [ctypes.POINTER(_Shape), _vp, _vp, ctypes.POINTER(_Layout),
+                                  _vp, _vp, _vp]
+_lib.moe_combine_send.restype = _i32
+
+
+def moe_dispatch_recv(shape: Shape, recv_x: torch.Tensor, recv_scales: Optional[torch.Tensor],
+                      layout: Layout, gemm_x: torch.Tensor, gemm_scales: Optional[torch.Tensor],
+                      gemm_offsets: torch.Tensor, stream=None) -> None:
+    """Receive half of dispatch: receive regions -> dense grouped-GEMM input."""
+    _check(_lib.moe_dispatch_recv(ctypes.byref(shape.c()), _ptr(recv_x), _ptr(recv_scales),
+                                  ctypes.byref(layout.c()), _ptr(gemm_x), _ptr(gemm_scales),
+                                  _ptr(gemm_offsets), _stream(stream)), "moe_dispatch_recv")
+
+
+def moe_combine_send(shape: Shape, gemm_y: torch.Tensor, gemm_scales: Optional[torch.Tensor],
+                     layout: Layout, expert_y: torch.Tensor,
+                     expert_scales: Optional[torch.Tensor], stream=None) -> None:
+    """Send half of the combine: dense expert outputs -> receive-region layout."""
+    _check(_lib.moe_combine_send(ctypes.byref(shape.c()), _ptr(gemm_y), _ptr(gemm_scales),
+                                 ctypes.byref(layout.c()), _ptr(expert_y), _ptr(expert_scales),
+                                 _stream(stream)), "moe_combine_send")
+
+
 def moe_status_string(status: int) -> str:
     return _lib.moe_status_string(status).decode()
 

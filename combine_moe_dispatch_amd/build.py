@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmoe_dispatch.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["capi.hip", "route_topk.hip", "dispatch.hip", "sources.hip", "combine.hip",
-           "combine_partial.hip",
+           "combine_partial.hip", "gemm_io.hip",
            "expert_scale.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

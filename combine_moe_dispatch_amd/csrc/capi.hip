@@ -226,6 +226,46 @@ moe_status moe_combine_partial_recv(const moe_shape* shape, const void* partial,
                                            shape->hidden, M, stream));
 }
 
+namespace {
+
+moe_status gemm_io(bool pack, const moe_shape* shape, const void* src, const float* src_scales,
+                   const moe_layout* layout, void* dst, float* dst_scales, int32_t* gemm_offsets,
+                   hipStream_t stream) {
+  int L;
+  int64_t rows;
+  moe_status st = check_shape(shape, &L, &rows);
+  if (st != MOE_OK) return st;
+  const bool fp8 = shape->payload == MOE_PAYLOAD_FP8_E4M3_B128;
+  if (!layout || !layout->expert_counts || !layout->expert_offsets || (pack && !gemm_offsets))
+    return MOE_ERR_INVALID_ARG;
+  const int64_t pairs = (int64_t)shape->num_tokens * shape->top_k;
+  if (pairs > 0) {
+    if (!src || !dst || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+    if (fp8 && (!src_scales || !dst_scales)) return MOE_ERR_INVALID_ARG;
+  }
+  return from_hip(moe::launch_gemm_io(pack, src, src_scales, dst, dst_scales,
+                                      layout->expert_counts, layout->expert_offsets, gemm_offsets,
+                                      (int)pairs, shape->num_experts, L, shape->rank_capacity,
+                                      shape->hidden, fp8 ? 1 : 0, stream));
+}
+
+}  // namespace
+
+moe_status moe_dispatch_recv(const moe_shape* shape, const void* recv_x, const float* recv_scales,
+                             const moe_layout* layout, void* gemm_x, float* gemm_scales,
+                             int32_t* gemm_offsets, hipStream_t stream) {
+  return gemm_io(true, shape, recv_x, recv_scales, layout, gemm_x, gemm_scales, gemm_offsets,
+                 stream);
+}
+
+moe_status moe_combine_send(const moe_shape* shape, const void* gemm_y, const float* gemm_scales,
+                            const moe_layout* layout, void* expert_y, float* expert_scales,
+                            hipStream_t stream) {
+  // the dense offsets are rebuilt on the device from the layout's counts
+  return gemm_io(false, shape, gemm_y, gemm_scales, layout, expert_y, expert_scales, nullptr,
+                 stream);
+}
+
 const char* moe_status_string(moe_status status) {
   switch (status) {
     case MOE_OK: return "MOE_OK";

@@ -60,6 +60,11 @@ hipError_t launch_combine_send(const void* y, const float* ys, const int32_t* to
 hipError_t launch_combine_recv(const void* partial, const int32_t* partial_rank, void* out,
                                int T, int H, int M, hipStream_t st);
 
+hipError_t launch_gemm_io(bool pack, const void* src, const float* src_scales, void* dst,
+                          float* dst_scales, const int32_t* counts, const int32_t* offsets,
+                          int32_t* dense_out, int max_rows, int E, int L, int C, int H,
+                          int payload, hipStream_t st);
+
 hipError_t launch_expert_scale(const void* recv, const float* recv_scales,
                                const int32_t* expert_counts, const int32_t* expert_offsets,
                                const float* alpha, void* y, float* y_scales, int E, int L,

@@ -215,6 +215,43 @@ moe_status moe_dispatch_sources(const moe_shape *shape, int32_t num_sources,
                                 hipStream_t stream);
 
 /*
+ * moe_dispatch_recv -- the receive half of dispatch: shuffle the tokens out of
+ * the receive regions into the tensor handed to the experts' grouped GEMM
+ * ([EFA] Dispatch and Combine: once all transfers are in, tokens are shuffled
+ * from the receive buffers into the grouped GEMM's input; [DSK] Quantization:
+ * kernels size their work from the routing counts, not the buffer bounds).
+ * moe_dispatch is the send half.
+ *
+ *   recv_x/recv_scales  as written by moe_dispatch (regions may have gaps).
+ *   layout        expert_counts and expert_offsets are read.
+ *   gemm_x        [T*k][H] dense rows out (bf16, or e4m3 codes), gemm_scales
+ *                 [T*k][H/128] for fp8 (else NULL): expert e's placed rows at
+ *                 [gemm_offsets[e], gemm_offsets[e+1]) in the order of its
+ *                 segment; rows past gemm_offsets[E] are not written.
+ *   gemm_offsets  [E+1] int32 out: exclusive prefix of the placed rows per
+ *                 expert (a segment may be cut short by its rank's capacity).
+ */
+moe_status moe_dispatch_recv(const moe_shape *shape, const void *recv_x,
+                             const float *recv_scales, const moe_layout *layout,
+                             void *gemm_x, float *gemm_scales, int32_t *gemm_offsets,
+                             hipStream_t stream);
+
+/*
+ * moe_combine_send -- the send half of the receiver-side combine: each
+ * expert's output rows go from the dense grouped-GEMM output back to the
+ * receive-region layout that moe_combine (the receive half) gathers from
+ * ([EFA] Send and Receive Buffers: the combine copies the tokens back with
+ * one write per peer).  The inverse of moe_dispatch_recv for the same layout.
+ *
+ *   gemm_y/gemm_scales  [T*k][H] dense rows as laid out by moe_dispatch_recv.
+ *   expert_y/expert_scales  receive-region layout out; rows no pair occupies
+ *                 are not written.
+ */
+moe_status moe_combine_send(const moe_shape *shape, const void *gemm_y,
+                            const float *gemm_scales, const moe_layout *layout,
+                            void *expert_y, float *expert_scales, hipStream_t stream);
+
+/*
  * moe_expert_scale -- stand-in for the experts' grouped GEMM between dispatch
  * and combine ([EFA] MoE all-to-all over EFA): every row of expert e's segment
  * is multiplied by alpha[e].  It reads the per-expert counts and offsets from

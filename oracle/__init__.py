@@ -294,6 +294,28 @@ def _combine(fn, y, y_scales, token_row, weights):
     return out
 
 
+def gemm_io(pack: bool, src: np.ndarray, src_scales, expert_counts, expert_offsets,
+            E: int, N: int, C: int, dst_rows: int, fill: int):
+    """Receive-side shuffle into the grouped GEMM's dense input (pack) or back
+    (EFA page, Dispatch and Combine).  src: [rows][row elements] uint16/uint8.
+    Returns (dst, dst_scales or None, dense offsets [E+1])."""
+    src = np.ascontiguousarray(src)
+    row_bytes = src.shape[1] * src.itemsize
+    dst = np.full((dst_rows, src.shape[1]), fill, src.dtype)
+    nb = 0 if src_scales is None else src_scales.shape[1]
+    ss = None if src_scales is None else _c(src_scales, np.float32)
+    ds = None if src_scales is None else np.full((dst_rows, nb), np.nan, np.float32)
+    dense = np.empty(E + 1, np.int32)
+    lib = _load()
+    lib.oracle_gemm_io.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 6 + [ctypes.c_int] * 5 + \
+        [ctypes.c_void_p]
+    lib.oracle_gemm_io.restype = None
+    lib.oracle_gemm_io(1 if pack else 0, _ptr(src), _ptr(ss), _ptr(dst), _ptr(ds),
+                       _ptr(_c(expert_counts, np.int32)), _ptr(_c(expert_offsets, np.int32)),
+                       E, N, C, row_bytes, nb, _ptr(dense))
+    return dst, ds, dense
+
+
 def combine_send(y, y_scales, token_row, ids, weights, E: int, N: int, exact: bool):
     """Sender-side partial reduction, stage 1 (EFA page, Evaluation): one bf16
     row per (token, distinct destination rank), ranks ascending.  Returns

@@ -543,3 +543,35 @@ void oracle_combine_recv(const uint16_t *partial, const int32_t *partial_rank,
       out[(size_t)t * H + c] = exact ? oracle_f64_to_bf16(accd) : oracle_f32_to_bf16(accf);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Receive-side shuffle (EFA page, Dispatch and Combine: once everything has */
+/* arrived, tokens are shuffled from the receive buffers into the tensor     */
+/* passed to the grouped GEMM), and its inverse for the combine.             */
+/* ------------------------------------------------------------------------ */
+void oracle_gemm_io(int pack, const uint8_t *src, const float *src_scales,
+                    uint8_t *dst, float *dst_scales, const int32_t *expert_counts,
+                    const int32_t *expert_offsets, int E, int N, int C,
+                    int row_bytes, int nb, int32_t *dense) {
+  const int L = E / N;
+  int32_t run = 0;
+  for (int e = 0; e < E; ++e) {
+    int32_t placed = expert_counts[e];
+    if (C > 0) {
+      int32_t room = (e / L) * C + C - expert_offsets[e];
+      if (room < 0) room = 0;
+      if (placed > room) placed = room;
+    }
+    dense[e] = run;
+    for (int32_t i = 0; i < placed; ++i) {
+      size_t region = (size_t)expert_offsets[e] + (size_t)i;
+      size_t packed = (size_t)run + (size_t)i;
+      size_t from = pack ? region : packed, to = pack ? packed : region;
+      memcpy(dst + to * (size_t)row_bytes, src + from * (size_t)row_bytes, (size_t)row_bytes);
+      if (src_scales)
+        memcpy(dst_scales + to * (size_t)nb, src_scales + from * (size_t)nb, sizeof(float) * (size_t)nb);
+    }
+    run += placed;
+  }
+  dense[E] = run;
+}

@@ -132,6 +132,17 @@ void oracle_combine_f32_ordered(const void *y, const float *y_scales,
                                 const int32_t *token_row, const float *w,
                                 int T, int k, int H, uint16_t *out);
 
+/* Receive-side shuffle into the grouped GEMM's input: expert e's placed rows
+ * (its count, cut short by its rank's capacity when C > 0) are copied, in
+ * segment order, to dense rows [dense[e], dense[e+1]); dense[] [E+1] is the
+ * exclusive prefix of the placed counts.  row_bytes per row; scales (nb per
+ * row) move along when non-NULL.  pack != 0: regions -> dense; pack == 0:
+ * dense -> regions (the combine's send half). */
+void oracle_gemm_io(int pack, const uint8_t *src, const float *src_scales,
+                    uint8_t *dst, float *dst_scales, const int32_t *expert_counts,
+                    const int32_t *expert_offsets, int E, int N, int C,
+                    int row_bytes, int nb, int32_t *dense);
+
 /* Sender-side partial reduction, stage 1: for token t, the distinct ranks of
  * its placed pairs in ascending order r_0 < r_1 < ... get partial slots
  * 0, 1, ... of M (M >= min(k, N)); slot i = bf16(sum over the pairs on rank

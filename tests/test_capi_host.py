@@ -144,3 +144,16 @@ def test_two_stage_combine_rejects_bad_arguments():
     assert recv(ctypes.byref(s), 16, 16, 24, None) == 1
     bad = api._Shape(4, 64, 9, 2, 2, 0, 0)
     assert recv(ctypes.byref(bad), 16, 16, 16, None) == 1
+
+
+def test_split_halves_reject_bad_arguments():
+    s = api._Shape(4, 64, 8, 2, 2, 0, 0)
+    lay = api._Layout(16, 16, 16, 16, 16, None, 16)
+    r, c = api._lib.moe_dispatch_recv, api._lib.moe_combine_send
+    assert r(ctypes.byref(s), 16, None, ctypes.byref(lay), 16, None, None, None) == 1  # offsets
+    assert r(ctypes.byref(s), 8, None, ctypes.byref(lay), 16, None, 16, None) == 1     # misaligned
+    assert r(ctypes.byref(s), 16, None, None, 16, None, 16, None) == 1
+    s8 = api._Shape(4, 128, 8, 2, 2, 0, 1)
+    assert r(ctypes.byref(s8), 16, None, ctypes.byref(lay), 16, None, 16, None) == 1  # scales
+    assert c(ctypes.byref(s), 16, None, ctypes.byref(lay), None, None, None) == 1
+    assert c(ctypes.byref(s8), 16, None, ctypes.byref(lay), 16, None, None) == 1
