@@ -65,6 +65,14 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   i = bi;
 }
 
+// Keep the two largest values seen (equal values fill both).
+__device__ __forceinline__ void top2_take(float l, float& m1, float& m2) {
+  const bool above1 = l > m1;
+  const bool above2 = l > m2;
+  m2 = above1 ? m1 : (above2 ? l : m2);
+  m1 = above1 ? l : m1;
+}
+
 // LDS hand-off inside one wavefront (no block barrier: waves exit early).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -77,7 +85,7 @@ __global__ void __launch_bounds__(kRouteWaves * kWave)
 route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bias, int T,
                   int E, int k, int score, int n_groups, int topk_groups,
                   int32_t* __restrict__ ids, float* __restrict__ weights) {
-  __shared__ float s_logit[GROUPED ? kRouteWaves : 1][GROUPED ? kMaxExperts : 1];
+  __shared__ __align__(16) float s_logit[GROUPED ? kRouteWaves : 1][GROUPED ? kMaxExperts : 1];
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int t = blockIdx.x * kRouteWaves + wave;
@@ -111,14 +119,25 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
     int gi = kNone;
     if (lane < n_groups) {
       float m1 = -INFINITY, m2 = -INFINITY;
-      for (int e = lane * gsz; e < lane * gsz + gsz; ++e) {
-        const float l = sl[e];
-        if (l > m1) {
-          m2 = m1;
-          m1 = l;
-        } else if (l > m2) {
-          m2 = l;
+      if ((gsz & 3) == 0) {
+        // 16-byte LDS reads, 4 in flight per round
+        const float4* g4 = reinterpret_cast<const float4*>(sl + lane * gsz);
+        for (int c0 = 0; c0 < gsz / 4; c0 += 4) {
+          float q[16];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float4 f = c0 + c < gsz / 4 ? g4[c0 + c]
+                                              : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            q[4 * c] = f.x;
+            q[4 * c + 1] = f.y;
+            q[4 * c + 2] = f.z;
+            q[4 * c + 3] = f.w;
+          }
+#pragma unroll
+          for (int c = 0; c < 16; ++c) top2_take(q[c], m1, m2);
         }
+      } else {
+        for (int e = lane * gsz; e < lane * gsz + gsz; ++e) top2_take(sl[e], m1, m2);
       }
       gv = gsz > 1 ? m1 + m2 : m1;
       gi = lane;

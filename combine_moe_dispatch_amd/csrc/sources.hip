@@ -43,18 +43,25 @@ source_counts_kernel(const int32_t* __restrict__ ids, int pairs_per_source, int 
   for (int e = threadIdx.x; e < E; e += kBlock) source_counts[(size_t)s * E + e] = hist[e];
 }
 
-// One thread per expert: source_offsets[e][s] = expert_offsets[e] + sum of
-// source_counts[s'][e] over s' < s.
+// One wave per expert, lanes over sources: source_offsets[e][s] =
+// expert_offsets[e] + sum of source_counts[s'][e] over s' < s, 64 sources per
+// DPP scan.
+constexpr int kWavesPerBlock = kBlock / kWave;
+
 __global__ void __launch_bounds__(kBlock)
 source_offsets_kernel(const int32_t* __restrict__ source_counts,
                       const int32_t* __restrict__ expert_offsets, int S, int E,
                       int32_t* __restrict__ source_offsets) {
-  const int e = blockIdx.x * kBlock + threadIdx.x;
-  if (e >= E) return;
+  const int e = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (e >= E) return;  // whole wave
+  const int lane = lane_id();
   int run = expert_offsets[e];
-  for (int s = 0; s < S; ++s) {
-    source_offsets[(size_t)e * S + s] = run;
-    run += source_counts[(size_t)s * E + e];
+  for (int s0 = 0; s0 < S; s0 += kWave) {
+    const int s = s0 + lane;
+    const int c = s < S ? source_counts[(size_t)s * E + e] : 0;
+    const int incl = wave_inclusive_sum_dpp(c);
+    if (s < S) source_offsets[(size_t)e * S + s] = run + incl - c;
+    run += __builtin_amdgcn_readlane(incl, kWave - 1);
   }
 }
 
@@ -67,8 +74,8 @@ hipError_t launch_source_metadata(const int32_t* ids, int S, int T, int k, int E
                      source_counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(source_offsets_kernel, dim3((E + kBlock - 1) / kBlock), dim3(kBlock), 0, st,
-                     source_counts, expert_offsets, S, E, source_offsets);
+  hipLaunchKernelGGL(source_offsets_kernel, dim3((E + kWavesPerBlock - 1) / kWavesPerBlock),
+                     dim3(kBlock), 0, st, source_counts, expert_offsets, S, E, source_offsets);
   return hipGetLastError();
 }
 
