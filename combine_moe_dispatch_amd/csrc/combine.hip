@@ -9,7 +9,7 @@
 // (8 at a time) and folds them with fp32 fused multiply-adds in slot order
 // from zero, then rounds to bf16 (nearest even) and stores 16 bytes.  The
 // gathers and the stores carry non-temporal (streaming) hints.  With
-// the fp8 payload a thread owns 16 columns: one 16-byte gather of codes per
+// the fp8 payload a thread owns 16 columns: two 8-byte gathers of codes per
 // row, each code decoded exactly to fp32 (the hardware OCP e4m3 convert) and
 // multiplied by its block's fp32 scale.  This is a bandwidth-bound gather-reduce: no MFMA.
 #include "device_common.h"
@@ -71,19 +71,27 @@ combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ tok
   store_stream(&out[(size_t)t * nvec + v], o);
 }
 
-// fp8: vectors of 16 codes; 8 vectors share one 128-column scale.
+// fp8: a lane owns two 8-code vectors, u and u + 64 of its block's 128, so
+// that each 16-byte bf16 store instruction of the wave covers 1 KB of the
+// output row without gaps (strided stores were measured to write back
+// partial lines: 1.67x the output bytes).  16 consecutive vectors share one
+// 128-column scale.  Workgroups are renumbered so that the column chunks of
+// one token run on one XCD and share the L2 lines of the token's scales.
 __global__ void __launch_bounds__(kBlock)
-combine_fp8_kernel(const uint4* __restrict__ y, const float* __restrict__ ys,
+combine_fp8_kernel(const uint2* __restrict__ y, const float* __restrict__ ys,
                    const int32_t* __restrict__ token_row, const float* __restrict__ w,
                    uint4* __restrict__ out, int H, int k, int col_chunks) {
-  const int t = blockIdx.x / col_chunks;
-  const int cc = blockIdx.x - t * col_chunks;
-  const int nvec = H / 16;
+  const unsigned b = xcd_local_block(blockIdx.x, gridDim.x);
+  const int t = b / col_chunks;
+  const int cc = b - t * col_chunks;
+  const int nv = H / 8;
   const int nb = H / kFp8Block;
-  const int v = cc * kBlock + threadIdx.x;
+  const int u0 = cc * 2 * kBlock + threadIdx.x;
+  const int u1 = u0 + kBlock;
   const int32_t* trow = token_row + (size_t)t * k;
   const float* tw = w + (size_t)t * k;
-  if (v >= nvec) return;
+  if (u0 >= nv) return;
+  const bool has1 = u1 < nv;
   float acc[16];
 #pragma unroll
   for (int m = 0; m < 16; ++m) acc[m] = 0.0f;
@@ -95,29 +103,37 @@ combine_fp8_kernel(const uint4* __restrict__ y, const float* __restrict__ ys,
       row[g] = j0 + g < k ? trow[j0 + g] : -1;
       wj[g] = j0 + g < k ? tw[j0 + g] : 0.0f;
     }
-    uint4 yv[kGroup];
-    float sc[kGroup];
+    uint2 c0[kGroup], c1[kGroup];
+    float s0[kGroup], s1[kGroup];
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
-      yv[g] = row[g] >= 0 ? load_stream(&y[(size_t)row[g] * nvec + v]) : make_uint4(0, 0, 0, 0);
-      sc[g] = row[g] >= 0 ? load_stream(&ys[(size_t)row[g] * nb + v / 8]) : 0.0f;
+      const bool on = row[g] >= 0;
+      const size_t r = on ? (size_t)row[g] : 0;
+      c0[g] = on ? load_stream(&y[r * nv + u0]) : make_uint2(0, 0);
+      c1[g] = on && has1 ? load_stream(&y[r * nv + u1]) : make_uint2(0, 0);
+      s0[g] = on ? load_stream(&ys[r * nb + u0 / 16]) : 0.0f;
+      s1[g] = on && has1 ? load_stream(&ys[r * nb + u1 / 16]) : 0.0f;
     }
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
       if (row[g] < 0) continue;
-      const uint32_t q[4] = {yv[g].x, yv[g].y, yv[g].z, yv[g].w};
       float dec[16];
+      e4m3x4_to_f32(c0[g].x, dec);
+      e4m3x4_to_f32(c0[g].y, dec + 4);
+      e4m3x4_to_f32(c1[g].x, dec + 8);
+      e4m3x4_to_f32(c1[g].y, dec + 12);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) e4m3x4_to_f32(q[m], dec + 4 * m);
+      for (int m = 0; m < 8; ++m) acc[m] = fmaf(wj[g], dec[m] * s0[g], acc[m]);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) acc[m] = fmaf(wj[g], dec[m] * sc[g], acc[m]);
+      for (int m = 8; m < 16; ++m) acc[m] = fmaf(wj[g], dec[m] * s1[g], acc[m]);
     }
   }
-  uint4* o = out + (size_t)t * (H / 8) + 2 * (size_t)v;
-  store_stream(&o[0], make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
-  store_stream(&o[1], make_uint4(pack_bf16x2(acc[8], acc[9]), pack_bf16x2(acc[10], acc[11]),
-                                 pack_bf16x2(acc[12], acc[13]), pack_bf16x2(acc[14], acc[15])));
+  uint4* o = out + (size_t)t * nv;
+  store_stream(&o[u0], make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                  pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
+  if (has1)
+    store_stream(&o[u1], make_uint4(pack_bf16x2(acc[8], acc[9]), pack_bf16x2(acc[10], acc[11]),
+                                    pack_bf16x2(acc[12], acc[13]), pack_bf16x2(acc[14], acc[15])));
 }
 
 }  // namespace
@@ -126,8 +142,8 @@ hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_r
                           const float* w, void* out, int T, int H, int k, int payload,
                           hipStream_t st) {
   if (T == 0) return hipSuccess;
-  const int nvec = payload == 0 ? H / 8 : H / 16;
-  const int col_chunks = (nvec + kBlock - 1) / kBlock;
+  const int per_block = payload == 0 ? kBlock : 2 * kBlock;  // vectors of 8 columns
+  const int col_chunks = (H / 8 + per_block - 1) / per_block;
   const unsigned blocks = (unsigned)T * (unsigned)col_chunks;
   if (payload == 0)
     hipLaunchKernelGGL(combine_bf16_kernel, dim3(blocks), dim3(kBlock), 0, st,
@@ -135,7 +151,7 @@ hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_r
                        reinterpret_cast<uint4*>(out), H, k, col_chunks);
   else
     hipLaunchKernelGGL(combine_fp8_kernel, dim3(blocks), dim3(kBlock), 0, st,
-                       reinterpret_cast<const uint4*>(y), ys, token_row, w,
+                       reinterpret_cast<const uint2*>(y), ys, token_row, w,
                        reinterpret_cast<uint4*>(out), H, k, col_chunks);
   return hipGetLastError();
 }

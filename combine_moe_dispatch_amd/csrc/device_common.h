@@ -73,6 +73,10 @@ __device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
   const u32x4 t = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
 }
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+  const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(t.x, t.y);
+}
 __device__ __forceinline__ void store_stream(uint2* p, uint2 v) {
   const u32x2 t = {v.x, v.y};
   __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
@@ -82,6 +86,17 @@ __device__ __forceinline__ float load_stream(const float* p) {
 }
 __device__ __forceinline__ void store_stream(float* p, float v) {
   __builtin_nontemporal_store(v, p);
+}
+
+// Workgroups are handed to the 8 XCDs of the chip in turn (workgroup b runs
+// on XCD b % 8), and each XCD has its own L2.  This renumbers the n
+// workgroups of a launch so that consecutive logical indices run on the same
+// XCD: logical = (workgroups on lower XCDs) + b / 8, a bijection onto [0, n).
+// Neighbouring tiles that share cache lines then share one L2.
+__device__ __forceinline__ unsigned xcd_local_block(unsigned b, unsigned n) {
+  constexpr unsigned kXcds = 8;
+  const unsigned x = b % kXcds, q = n / kXcds, r = n % kXcds;
+  return x * q + (x < r ? x : r) + b / kXcds;
 }
 
 // Inclusive/exclusive sums over a wave64 with shuffles.
