@@ -13,8 +13,9 @@ uses of a set exceed twice the 256 MB Infinity Cache.  Warm: one set, reused
 (cache-assisted), reported alongside.
 
 Timing: HIP graphs of back-to-back launches replayed between HIP events on the
-launch stream.  The step figure captures K whole steps; each kernel's average
-launch duration comes from a graph of K launches of that kernel alone.
+launch stream.  The step figure captures K whole steps (one timed replay);
+each kernel's average launch duration comes from a graph of K launches of that
+kernel alone (median of three timed replays).
 
 Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -223,18 +224,22 @@ def run_gpu(args, w, inp):
                     fn(s)
         return g
 
-    def time_graph(g, n):
+    def time_graph(g, n, reps=1):
         # replay() launches on torch's current stream: make that the launch
-        # stream, and bracket the replay with events recorded on it
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / n  # us per unit
+        # stream, and bracket the replay with events recorded on it.  With
+        # reps > 1 the median of that many timed replays is returned.
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / n)  # us per unit
+        return sorted(ts)[len(ts) // 2]
 
     K, W = args.steps, args.warmup
     res = {"sets": S, "status": status, "partial_rows": partial_rows}
@@ -257,9 +262,9 @@ def run_gpu(args, w, inp):
         step_us = time_graph(g_step, K)
         r = {
             "step_us": step_us,
-            "route_us": time_graph(g_route, K),
-            "dispatch_us": time_graph(g_disp, K),
-            "combine_us": time_graph(g_comb, K),
+            "route_us": time_graph(g_route, K, reps=3),
+            "dispatch_us": time_graph(g_disp, K, reps=3),
+            "combine_us": time_graph(g_comb, K, reps=3),
         }
         if two_stage:
             g_send = capture([combine_send], K, rotate)
@@ -267,8 +272,8 @@ def run_gpu(args, w, inp):
             with torch.cuda.stream(stream):
                 g_send.replay()
                 g_recv.replay()
-            r["combine_send_us"] = time_graph(g_send, K)
-            r["combine_recv_us"] = time_graph(g_recv, K)
+            r["combine_send_us"] = time_graph(g_send, K, reps=3)
+            r["combine_recv_us"] = time_graph(g_recv, K, reps=3)
             del g_send, g_recv
         res[mode] = r
         del g_step, g_route, g_disp, g_comb

@@ -13,9 +13,10 @@
 // order from 0).
 //
 // A one-wave block owns (token, 64-vector column chunk).  Lane j holds slot
-// j's row, rank and weight; the rank grouping is a few readlanes; rows stream
-// in 8 at a time and are folded into up to GC group accumulators (more
-// groups take more passes).
+// j's row, rank and weight; the rank grouping is a few readlanes.  With
+// k <= 8 all k rows are loaded at once and the groups are folded and stored
+// one after the other; with larger k rows stream in 8 at a time and are
+// folded into up to GC group accumulators (more groups take more passes).
 #include "device_common.h"
 #include "launch.h"
 
@@ -34,6 +35,150 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
+// Lane j < k: slot j's row, rank (-1 if skipped), weight and group (the
+// index of its rank among the token's distinct ranks in ascending order);
+// returns m, the number of distinct ranks.  Block (t, chunk 0) also writes
+// partial_rank[t][:].
+__device__ __forceinline__ int slot_groups(const int32_t* __restrict__ token_row,
+                                           const int32_t* __restrict__ ids,
+                                           const float* __restrict__ w,
+                                           int32_t* __restrict__ partial_rank, int t, int cc,
+                                           int k, int E, int L, int M, int& my_row,
+                                           float& my_w, int& my_group) {
+  const int lane = threadIdx.x;
+  int my_rank = -1;
+  my_row = -1;
+  my_w = 0.0f;
+  if (lane < k) {
+    my_row = token_row[(size_t)t * k + lane];
+    const int e = ids[(size_t)t * k + lane];
+    my_rank = (my_row >= 0 && (unsigned)e < (unsigned)E) ? e / L : -1;
+    my_w = w[(size_t)t * k + lane];
+  }
+  // first slot of each rank, the number of distinct ranks, and each slot's group
+  bool first = my_rank >= 0;
+  for (int j = 0; j < k; ++j)
+    if (j < lane && __builtin_amdgcn_readlane(my_rank, j) == my_rank) first = false;
+  const uint64_t firsts = __ballot(first);
+  const int m = popc64(firsts);
+  my_group = -1;
+  if (my_rank >= 0) {
+    my_group = 0;
+    for (int j = 0; j < k; ++j)
+      if (((firsts >> j) & 1ull) && __builtin_amdgcn_readlane(my_rank, j) < my_rank) ++my_group;
+  }
+  if (cc == 0 && lane < M) {
+    int r = -1;
+    for (int j = 0; j < k; ++j)
+      if (__builtin_amdgcn_readlane(my_group, j) == lane) r = __builtin_amdgcn_readlane(my_rank, j);
+    partial_rank[(size_t)t * M + lane] = r;
+  }
+  return m;
+}
+
+// bf16 partial row store of 8 or 16 fp32 sums (one or two 16-byte vectors).
+template <int COLS>
+__device__ __forceinline__ void store_partial(uint4* dst, const float* acc) {
+#pragma unroll
+  for (int h = 0; h < COLS / 8; ++h)
+    store_stream(&dst[h], make_uint4(pack_bf16x2(acc[8 * h + 0], acc[8 * h + 1]),
+                                     pack_bf16x2(acc[8 * h + 2], acc[8 * h + 3]),
+                                     pack_bf16x2(acc[8 * h + 4], acc[8 * h + 5]),
+                                     pack_bf16x2(acc[8 * h + 6], acc[8 * h + 7])));
+}
+
+// k <= kGroup: all k rows are loaded at once into registers, then each group
+// is folded (its slots in slot order) and stored in turn.  A lane owns KV
+// vectors of 8 columns, u and u + 64 (fp8: KV = 2, 8-byte code loads), so
+// every 16-byte store instruction of the wave covers 1 KB of a partial row
+// without gaps.  fp8 workgroups are renumbered so the column chunks of one
+// token share an XCD and the L2 lines of its scales.
+template <bool FP8>
+__global__ void __launch_bounds__(kBlock)
+combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ ys,
+                          const int32_t* __restrict__ token_row,
+                          const int32_t* __restrict__ ids, const float* __restrict__ w,
+                          uint4* __restrict__ partial, int32_t* __restrict__ partial_rank,
+                          int H, int k, int E, int L, int M, int col_chunks) {
+  constexpr int KV = FP8 ? 2 : 1;
+  const unsigned b = FP8 ? xcd_local_block(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int t = b / col_chunks;
+  const int cc = b - t * col_chunks;
+  const int nv = H / 8;  // 8-column vectors per row
+  const int nb = H / kFp8Block;
+  int u[KV];
+#pragma unroll
+  for (int i = 0; i < KV; ++i) u[i] = cc * kBlock * KV + (int)threadIdx.x + i * kBlock;
+  int my_row, my_group;
+  float my_w;
+  const int m = slot_groups(token_row, ids, w, partial_rank, t, cc, k, E, L, M, my_row, my_w,
+                            my_group);
+  // every slot's group, row and weight as wave-uniform values, read while
+  // all lanes are still active
+  int grp[kGroup], rj[kGroup];
+  float wj[kGroup];
+#pragma unroll
+  for (int g = 0; g < kGroup; ++g) {
+    grp[g] = g < k ? __builtin_amdgcn_readlane(my_group, g) : -1;
+    rj[g] = g < k ? __builtin_amdgcn_readlane(my_row, g) : -1;
+    wj[g] = g < k ? readlane_f(my_w, g) : 0.0f;
+  }
+  if (u[0] >= nv) return;
+  // raw loads of every slot's vectors; each is decoded once, in its group
+  uint4 yv[kGroup];      // bf16: 8 values
+  uint2 cv[kGroup][KV];  // fp8: 8 codes per vector
+  float sc[kGroup][KV];
+  if constexpr (FP8) {
+    const uint2* y8 = reinterpret_cast<const uint2*>(y);
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+      for (int i = 0; i < KV; ++i) {
+        const bool use = grp[g] >= 0 && u[i] < nv;
+        const size_t r = use ? (size_t)rj[g] : 0;
+        cv[g][i] = use ? load_stream(&y8[r * nv + u[i]]) : make_uint2(0, 0);
+        sc[g][i] = use ? load_stream(&ys[r * nb + u[i] / 16]) : 0.0f;
+      }
+  } else {
+    const uint4* y16 = reinterpret_cast<const uint4*>(y);
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g)
+      yv[g] = grp[g] >= 0 ? load_stream(&y16[(size_t)rj[g] * nv + u[0]]) : make_uint4(0, 0, 0, 0);
+  }
+  for (int q = 0; q < m; ++q) {
+    float acc[8 * KV];
+#pragma unroll
+    for (int c = 0; c < 8 * KV; ++c) acc[c] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      if (grp[g] != q) continue;
+      float val[8 * KV];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+          e4m3x4_to_f32(cv[g][i].x, &val[8 * i]);
+          e4m3x4_to_f32(cv[g][i].y, &val[8 * i + 4]);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) val[8 * i + c] = val[8 * i + c] * sc[g][i];
+        }
+      } else {
+        const uint32_t q4[4] = {yv[g].x, yv[g].y, yv[g].z, yv[g].w};
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          val[2 * c4] = bf16_lo(q4[c4]);
+          val[2 * c4 + 1] = bf16_hi(q4[c4]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8 * KV; ++c) acc[c] = fmaf(wj[g], val[c], acc[c]);
+    }
+    uint4* dst = partial + ((size_t)t * M + q) * nv;
+#pragma unroll
+    for (int i = 0; i < KV; ++i)
+      if (u[i] < nv) store_partial<8>(&dst[u[i]], &acc[8 * i]);
+  }
+}
+
 template <bool FP8, int GC>
 __global__ void __launch_bounds__(kBlock)
 combine_send_kernel(const uint4* __restrict__ y, const float* __restrict__ ys,
@@ -47,34 +192,10 @@ combine_send_kernel(const uint4* __restrict__ y, const float* __restrict__ ys,
   const int nvec = H / kCols;
   const int lane = threadIdx.x;
   const int v = cc * kBlock + lane;
-  // lane j < k: slot j's row, rank (-1 if skipped) and weight
-  int my_row = -1, my_rank = -1;
-  float my_w = 0.0f;
-  if (lane < k) {
-    my_row = token_row[(size_t)t * k + lane];
-    const int e = ids[(size_t)t * k + lane];
-    my_rank = (my_row >= 0 && (unsigned)e < (unsigned)E) ? e / L : -1;
-    my_w = w[(size_t)t * k + lane];
-  }
-  // first slot of each rank, the number of distinct ranks, and each slot's
-  // group = the index of its rank among the distinct ranks in ascending order
-  bool first = my_rank >= 0;
-  for (int j = 0; j < k; ++j)
-    if (j < lane && __builtin_amdgcn_readlane(my_rank, j) == my_rank) first = false;
-  const uint64_t firsts = __ballot(first);
-  const int m = popc64(firsts);
-  int my_group = -1;
-  if (my_rank >= 0) {
-    my_group = 0;
-    for (int j = 0; j < k; ++j)
-      if (((firsts >> j) & 1ull) && __builtin_amdgcn_readlane(my_rank, j) < my_rank) ++my_group;
-  }
-  if (cc == 0 && lane < M) {
-    int r = -1;
-    for (int j = 0; j < k; ++j)
-      if (__builtin_amdgcn_readlane(my_group, j) == lane) r = __builtin_amdgcn_readlane(my_rank, j);
-    partial_rank[(size_t)t * M + lane] = r;
-  }
+  int my_row, my_group;
+  float my_w;
+  const int m = slot_groups(token_row, ids, w, partial_rank, t, cc, k, E, L, M, my_row, my_w,
+                            my_group);
   // lanes past the row end stay alive: later slots' values are read from
   // every lane with readlane
   const bool active = v < nvec;
@@ -129,13 +250,8 @@ combine_send_kernel(const uint4* __restrict__ y, const float* __restrict__ ys,
 #pragma unroll
     for (int q = 0; q < GC; ++q) {
       if (!active || g0 + q >= m) continue;
-      uint4* dst = partial + ((size_t)t * M + g0 + q) * (H / 8) + (size_t)v * (kCols / 8);
-#pragma unroll
-      for (int h = 0; h < kCols / 8; ++h)
-        store_stream(&dst[h], make_uint4(pack_bf16x2(acc[q][8 * h + 0], acc[q][8 * h + 1]),
-                                         pack_bf16x2(acc[q][8 * h + 2], acc[q][8 * h + 3]),
-                                         pack_bf16x2(acc[q][8 * h + 4], acc[q][8 * h + 5]),
-                                         pack_bf16x2(acc[q][8 * h + 6], acc[q][8 * h + 7])));
+      store_partial<kCols>(partial + ((size_t)t * M + g0 + q) * (H / 8) + (size_t)v * (kCols / 8),
+                           acc[q]);
     }
   }
 }
@@ -188,6 +304,21 @@ hipError_t launch_combine_send(const void* y, const float* ys, const int32_t* to
   const int nvec = payload == 0 ? H / 8 : H / 16;
   const int col_chunks = (nvec + kBlock - 1) / kBlock;
   const unsigned blocks = (unsigned)T * (unsigned)col_chunks;
+  const int L = E / N;
+  if (k <= kGroup) {
+    // 64 vectors of 8 columns per block (bf16), 128 (fp8)
+    const int chunks = (H / 8 + kBlock * (payload ? 2 : 1) - 1) / (kBlock * (payload ? 2 : 1));
+    const unsigned nblk = (unsigned)T * (unsigned)chunks;
+    if (payload == 0)
+      hipLaunchKernelGGL((combine_send_small_kernel<false>), dim3(nblk), dim3(kBlock), 0, st, y,
+                         ys, token_row, ids, w, reinterpret_cast<uint4*>(partial), partial_rank,
+                         H, k, E, L, M, chunks);
+    else
+      hipLaunchKernelGGL((combine_send_small_kernel<true>), dim3(nblk), dim3(kBlock), 0, st, y,
+                         ys, token_row, ids, w, reinterpret_cast<uint4*>(partial), partial_rank,
+                         H, k, E, L, M, chunks);
+    return hipGetLastError();
+  }
   if (payload == 0)
     hipLaunchKernelGGL((combine_send_kernel<false, 8>), dim3(blocks), dim3(kBlock), 0, st,
                        reinterpret_cast<const uint4*>(y), ys, token_row, ids, w,

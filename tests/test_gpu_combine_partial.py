@@ -25,6 +25,7 @@ pytestmark = pytest.mark.gpu
     (64, 1024, 32, 16, 16, 0, 0, False),       # up to 16 ranks per token: two passes
     (64, 512, 32, 16, 16, 0, 1, False),        # fp8, up to 16 ranks: four passes
     (100, 256, 16, 4, 4, 60, 0, True),         # capacity-skipped pairs
+    (50, 536, 64, 8, 8, 0, 0, False),          # ragged row: last chunk has 3 live lanes < k
     (0, 256, 16, 4, 4, 0, 0, False),           # no tokens
 ])
 def test_two_stage_combine(T, H, E, k, N, C, payload, skew):
