@@ -81,9 +81,20 @@ def nbytes_row(w):
     return w.H + 4 * (w.H // 128) if w.payload == "fp8" else 2 * w.H
 
 
-def source_sha():
+# Sources that define each step's kernels (plus those every kernel shares):
+# a PMC figure stays valid while these are unchanged.
+KERNEL_SOURCES = {
+    "route": ["route_topk.hip"],
+    "dispatch": ["dispatch.hip", "sources.hip"],
+    "combine": ["combine.hip", "combine_partial.hip"],
+}
+SHARED_SOURCES = ["device_common.h", "launch.h", "capi.hip"]
+
+
+def source_sha(part):
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "combine_moe_dispatch_amd", "csrc", "*")))
+    csrc = os.path.join(ROOT, "combine_moe_dispatch_amd", "csrc")
+    files = [os.path.join(csrc, f) for f in KERNEL_SOURCES[part] + SHARED_SOURCES]
     files.append(os.path.join(ROOT, "include", "moe_dispatch.h"))
     for f in files:
         h.update(open(f, "rb").read())
@@ -111,7 +122,7 @@ def read_traffic(tag, kernel):
         if "=" in line and not line.startswith("#"):
             a, b = line.split("=", 1)
             kv[a.strip()] = b.strip()
-    if kv.get("source_sha") != source_sha():
+    if kv.get(f"{kernel}_source_sha") != source_sha(kernel):
         return None
     val = kv.get(f"{kernel}_traffic_bytes_per_launch")
     return None if val is None else float(val)

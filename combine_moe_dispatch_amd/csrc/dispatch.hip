@@ -129,8 +129,19 @@ __device__ __forceinline__ void store_bf16(const DispatchParams& p, int v0, int 
   }
 }
 
-// fp8: a vector is 8 columns; 16 consecutive lanes hold one 128-column block
-// (v0 and v1 are multiples of 16, so a group is all in or all out).
+// Max over each 16-lane DPP row: lane ^ 1, lane ^ 2, then the mirrored
+// quad and the mirrored half-row, so every lane ends with the row's max.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false)));
+  return v;
+}
+
+// fp8: a vector is 8 columns; 16 consecutive lanes (one DPP row) hold one
+// 128-column block (v0 and v1 are multiples of 16, so a group is all in or
+// all out).
 template <int MAXV>
 __device__ __forceinline__ void store_fp8(const DispatchParams& p, int v0, int v1,
                                           const uint4 (&xv)[MAXV], int row_lane) {
@@ -148,8 +159,7 @@ __device__ __forceinline__ void store_fp8(const DispatchParams& p, int v0, int v
     float amax = 0.0f;
 #pragma unroll
     for (int m = 0; m < 8; ++m) amax = fmaxf(amax, fabsf(f[m]));
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, kWave));
+    amax = row16_max(amax);
     if (v >= v1) continue;
     const float s = amax / 448.0f;
     uint32_t lo = 0, hi = 0;
