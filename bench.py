@@ -10,7 +10,9 @@ resident in HBM before the timed region.
 
 Cold (headline): S buffer sets rotate so that the bytes touched between two
 uses of a set exceed twice the 256 MB Infinity Cache.  Warm: one set, reused
-(cache-assisted), reported alongside.
+(cache-assisted), reported alongside.  Stream floor: plain streaming read and
+write kernels (libmoe_ceiling.so) over the payload size, timed the same way,
+give what the memory system sustains at that size.
 
 Timing: HIP graphs of back-to-back launches replayed between HIP events on the
 launch stream.  The step figure captures K whole steps (one timed replay);
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true")
+    ap.add_argument("--no-floor", action="store_true",
+                    help="skip the streaming read/write floor at the payload size")
     ap.add_argument("--groups", type=int, default=1,
                     help="route with group-limited top-k over this many expert groups")
     ap.add_argument("--topk-groups", type=int, default=1, help="groups kept per token")
@@ -288,7 +292,58 @@ def run_gpu(args, w, inp):
             del g_send, g_recv
         res[mode] = r
         del g_step, g_route, g_disp, g_comb
+    if not args.no_floor:
+        res["floor"] = stream_floor(torch, stream, time_graph, payload_bytes(w), min(K, 100))
     return res
+
+
+def payload_bytes(w):
+    """Payload bytes one dispatch writes (and one combine reads): k rows per token."""
+    row = 2 * w.H if w.payload == "bf16" else w.H + 4 * (w.H // 128)
+    return w.tokens * w.k * row
+
+
+def stream_floor(torch, stream, time_graph, nbytes, n):
+    """What the memory system sustains at this size: plain streaming read and
+    write of `nbytes` with the same 16-byte non-temporal accesses, and an
+    empty launch, timed like the kernels (graphs of n launches over rotating
+    buffers, cold); the best of three grid sizes."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "combine_moe_dispatch_amd", "libmoe_ceiling.so"))
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.moe_ceiling_read.argtypes = [vp, sz, vp, i32, vp]
+    lib.moe_ceiling_write.argtypes = [vp, sz, i32, vp]
+    lib.moe_ceiling_empty.argtypes = [vp]
+    nbytes = (nbytes + 15) // 16 * 16
+    S = min(64, max(2, math.ceil(2 * MALL_BYTES / nbytes)))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(S)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.zeros(65536, dtype=torch.int32, device="cuda")
+    nvec = nbytes // 16
+    st = stream.cuda_stream
+
+    def timed(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                assert fn(i) == 0
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        t = time_graph(g, n, reps=3)
+        del g
+        return t
+
+    grids = (1024, 2048, 4096)
+    rd = min(timed(lambda i, b=b: lib.moe_ceiling_read(bufs[i % S].data_ptr(), nvec,
+                                                       sink.data_ptr(), b, st)) for b in grids)
+    wr = min(timed(lambda i, b=b: lib.moe_ceiling_write(bufs[i % S].data_ptr(), nvec, b, st))
+             for b in grids)
+    em = timed(lambda i: lib.moe_ceiling_empty(st))
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "read_us": rd, "write_us": wr, "empty_launch_us": em}
 
 
 def cpu_baseline(w, inp, seconds):
@@ -424,6 +479,15 @@ def main():
             "dispatch_us": round(wm["dispatch_us"], 3), "combine_us": round(wm["combine_us"], 3),
             "route_us": round(wm["route_us"], 3), "step_us": round(wm["step_us"], 3),
             "GBps": round(dc_bytes / (wus * 1e-6) / 1e9, 2)}
+    if "floor" in g:
+        fl = g["floor"]
+        line["stream_floor"] = {
+            "payload_bytes": fl["bytes"], "read_us": round(fl["read_us"], 3),
+            "write_us": round(fl["write_us"], 3), "empty_launch_us": round(fl["empty_launch_us"], 3),
+            "read_GBps": round(fl["bytes"] / (fl["read_us"] * 1e-6) / 1e9, 1),
+            "write_GBps": round(fl["bytes"] / (fl["write_us"] * 1e-6) / 1e9, 1),
+            "dispatch_over_write_floor": round(cold["dispatch_us"] / fl["write_us"], 3),
+            "combine_over_read_floor": round(cold["combine_us"] / fl["read_us"], 3)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

@@ -111,8 +111,8 @@ combine_fp8_kernel(const uint2* __restrict__ y, const float* __restrict__ ys,
       const size_t r = on ? (size_t)row[g] : 0;
       c0[g] = on ? load_stream(&y[r * nv + u0]) : make_uint2(0, 0);
       c1[g] = on && has1 ? load_stream(&y[r * nv + u1]) : make_uint2(0, 0);
-      s0[g] = on ? load_stream(&ys[r * nb + u0 / 16]) : 0.0f;
-      s1[g] = on && has1 ? load_stream(&ys[r * nb + u1 / 16]) : 0.0f;
+      s0[g] = on ? ys[r * nb + u0 / 16] : 0.0f;  // scales: cached loads
+      s1[g] = on && has1 ? ys[r * nb + u1 / 16] : 0.0f;
     }
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {

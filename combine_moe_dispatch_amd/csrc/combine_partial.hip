@@ -137,7 +137,7 @@ combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ 
         const bool use = grp[g] >= 0 && u[i] < nv;
         const size_t r = use ? (size_t)rj[g] : 0;
         cv[g][i] = use ? load_stream(&y8[r * nv + u[i]]) : make_uint2(0, 0);
-        sc[g][i] = use ? load_stream(&ys[r * nb + u[i] / 16]) : 0.0f;
+        sc[g][i] = use ? ys[r * nb + u[i] / 16] : 0.0f;  // scales: cached loads
       }
   } else {
     const uint4* y16 = reinterpret_cast<const uint4*>(y);
@@ -216,7 +216,7 @@ combine_send_kernel(const uint4* __restrict__ y, const float* __restrict__ ys,
         const int rj = j < k ? __builtin_amdgcn_readlane(my_row, j) : -1;
         const bool use = active && gj >= g0 && gj < g0 + GC;
         yv[g] = use ? load_stream(&y[(size_t)rj * nvec + v]) : make_uint4(0, 0, 0, 0);
-        sc[g] = (FP8 && use) ? load_stream(&ys[(size_t)rj * nb + v / 8]) : 0.0f;
+        sc[g] = (FP8 && use) ? ys[(size_t)rj * nb + v / 8] : 0.0f;
       }
 #pragma unroll
       for (int g = 0; g < kGroup; ++g) {

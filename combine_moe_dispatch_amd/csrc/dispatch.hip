@@ -31,9 +31,11 @@
 //    block turns the chunk histograms into per-chunk bases and the global
 //    metadata; (3) the scatter reads a pair's row from those.
 //
-// Rows move as 16-byte vectors with non-temporal (streaming) hints; with the fp8 payload each group of 16 lanes
-// owns one 128-column block, reduces its amax with in-group shuffles and
-// stores 8 codes per lane plus one scale per block and destination.
+// Rows move as 16-byte vectors with non-temporal (streaming) hints.  With the
+// fp8 payload a lane owns 16 columns and each group of 8 lanes one 128-column
+// block: the group reduces its amax with DPP, each lane stores its 16 codes
+// as one 16-byte vector, and the group's first lane the block's scale, per
+// destination row.
 #include "device_common.h"
 #include "launch.h"
 
@@ -100,21 +102,36 @@ __device__ void write_metadata(const DispatchParams& p, const int* cnt, const in
 // wave, lane j < k holds the row of slot j (-1 = skipped); the store loop
 // reads it with readlane, so no LDS staging or barrier is needed.
 // ---------------------------------------------------------------------------
-template <int MAXV>
-__device__ __forceinline__ void load_slice(const DispatchParams& p, int t, int v0, int v1,
-                                           uint4 (&xv)[MAXV]) {
-  const int nvec = p.H / 8;
-  const uint4* x = reinterpret_cast<const uint4*>(p.x) + (size_t)t * nvec;
+// A thread's unit of a row: 8 columns (one 16-byte bf16 vector) for the bf16
+// payload, 16 columns (two bf16 vectors in, one 16-byte vector of codes out)
+// for fp8.
+template <int PAYLOAD>
+struct Unit {
+  static constexpr int kXV = PAYLOAD ? 2 : 1;  // 16-byte x vectors per unit
+  static constexpr int kCols = 8 * kXV;
+};
+
+__host__ __device__ __forceinline__ int units_per_row(const DispatchParams& p) {
+  return p.H / (p.payload ? 16 : 8);
+}
+
+template <int PAYLOAD, int MAXV>
+__device__ __forceinline__ void load_slice(const DispatchParams& p, int t, int u0, int u1,
+                                           uint4 (&xv)[MAXV][Unit<PAYLOAD>::kXV]) {
+  constexpr int kXV = Unit<PAYLOAD>::kXV;
+  const uint4* x = reinterpret_cast<const uint4*>(p.x) + (size_t)t * (p.H / 8);
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
-    const int v = v0 + threadIdx.x + i * kBlock;
-    xv[i] = v < v1 ? load_stream(&x[v]) : make_uint4(0, 0, 0, 0);
+    const int u = u0 + threadIdx.x + i * kBlock;
+#pragma unroll
+    for (int c = 0; c < kXV; ++c)
+      xv[i][c] = u < u1 ? load_stream(&x[kXV * u + c]) : make_uint4(0, 0, 0, 0);
   }
 }
 
 template <int MAXV>
-__device__ __forceinline__ void store_bf16(const DispatchParams& p, int v0, int v1,
-                                           const uint4 (&xv)[MAXV], int row_lane) {
+__device__ __forceinline__ void store_bf16(const DispatchParams& p, int u0, int u1,
+                                           const uint4 (&xv)[MAXV][1], int row_lane) {
   const int nvec = p.H / 8;
   uint4* recv = reinterpret_cast<uint4*>(p.recv);
   for (int j = 0; j < p.k; ++j) {
@@ -123,60 +140,76 @@ __device__ __forceinline__ void store_bf16(const DispatchParams& p, int v0, int 
     uint4* dst = recv + (size_t)row * nvec;
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
-      const int v = v0 + threadIdx.x + i * kBlock;
-      if (v < v1) store_stream(&dst[v], xv[i]);
+      const int u = u0 + threadIdx.x + i * kBlock;
+      if (u < u1) store_stream(&dst[u], xv[i][0]);
     }
   }
 }
 
-// Max over each 16-lane DPP row: lane ^ 1, lane ^ 2, then the mirrored
-// quad and the mirrored half-row, so every lane ends with the row's max.
-__device__ __forceinline__ float row16_max(float v) {
+// Max over each group of 8 lanes (half of a DPP row): lane ^ 1, lane ^ 2,
+// then the mirrored quad, so every lane ends with its group's max.
+__device__ __forceinline__ float lanes8_max(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false)));
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false)));
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false)));
   return v;
 }
 
-// fp8: a vector is 8 columns; 16 consecutive lanes (one DPP row) hold one
-// 128-column block (v0 and v1 are multiples of 16, so a group is all in or
-// all out).
+// fp8: a unit is 16 columns; 8 consecutive lanes hold one 128-column block
+// (u0 and u1 are multiples of 8, so a group is all in or all out).  Each
+// lane stores its 16 codes as one 16-byte vector, the group's first lane the
+// block's scale.
 template <int MAXV>
-__device__ __forceinline__ void store_fp8(const DispatchParams& p, int v0, int v1,
-                                          const uint4 (&xv)[MAXV], int row_lane) {
+__device__ __forceinline__ void store_fp8(const DispatchParams& p, int u0, int u1,
+                                          const uint4 (&xv)[MAXV][2], int row_lane) {
   const int nb = p.H / kFp8Block;
+  const int nu = p.H / 16;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
-    const int v = v0 + threadIdx.x + i * kBlock;
-    float f[8];
-    const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+    const int u = u0 + threadIdx.x + i * kBlock;
+    float f[16];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      f[2 * m] = bf16_lo(w4[m]);
-      f[2 * m + 1] = bf16_hi(w4[m]);
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t w4[4] = {xv[i][c].x, xv[i][c].y, xv[i][c].z, xv[i][c].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f[8 * c + 2 * m] = bf16_lo(w4[m]);
+        f[8 * c + 2 * m + 1] = bf16_hi(w4[m]);
+      }
     }
     float amax = 0.0f;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) amax = fmaxf(amax, fabsf(f[m]));
-    amax = row16_max(amax);
-    if (v >= v1) continue;
+    for (int m = 0; m < 16; ++m) amax = fmaxf(amax, fabsf(f[m]));
+    amax = lanes8_max(amax);
+    if (u >= u1) continue;
     const float s = amax / 448.0f;
-    uint32_t lo = 0, hi = 0;
+    uint32_t code[4] = {0, 0, 0, 0};
     if (amax != 0.0f) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) lo |= f32_to_e4m3(f[m] / s) << (8 * m);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) hi |= f32_to_e4m3(f[4 + m] / s) << (8 * m);
+      for (int m = 0; m < 16; ++m) code[m / 4] |= f32_to_e4m3(f[m] / s) << (8 * (m % 4));
     }
+    const uint4 cv = make_uint4(code[0], code[1], code[2], code[3]);
     for (int j = 0; j < p.k; ++j) {
       const int row = __builtin_amdgcn_readlane(row_lane, j);
       if (row < 0) continue;
-      uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(p.recv) + (size_t)row * p.H);
-      store_stream(&dst[v], make_uint2(lo, hi));
-      if ((threadIdx.x & 15) == 0) store_stream(&p.recv_scales[(size_t)row * nb + v / 16], s);
+      uint4* dst = reinterpret_cast<uint4*>(p.recv) + (size_t)row * nu;
+      store_stream(&dst[u], cv);
+      // scales are plain stores: a wave writes only 32 bytes of a row's
+      // scales, and the L2 merges the pieces of one row into whole lines
+      // (measured faster than streaming them)
+      if ((threadIdx.x & 7) == 0) p.recv_scales[(size_t)row * nb + u / 8] = s;
     }
   }
+}
+
+template <int PAYLOAD, int MAXV>
+__device__ __forceinline__ void store_slice(const DispatchParams& p, int u0, int u1,
+                                            const uint4 (&xv)[MAXV][Unit<PAYLOAD>::kXV],
+                                            int row_lane) {
+  if constexpr (PAYLOAD == 0)
+    store_bf16<MAXV>(p, u0, u1, xv, row_lane);
+  else
+    store_fp8<MAXV>(p, u0, u1, xv, row_lane);
 }
 
 // Block (t, cc == 0), wave 0, lanes j < k publish the rows of token t.
@@ -260,9 +293,8 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   const int b = blockIdx.x - 1;
   const int t = b / p.col_chunks;
   const int cc = b - t * p.col_chunks;
-  const int nvec = p.H / 8;
-  const int v0 = cc * p.vec_per_chunk;
-  const int v1 = min(v0 + p.vec_per_chunk, nvec);
+  const int u0 = cc * p.vec_per_chunk;
+  const int u1 = min(u0 + p.vec_per_chunk, units_per_row(p));
 
   // issue every load first: this token's k ids, the whole id list (a few
   // per thread) and this block's slice of the token row
@@ -273,8 +305,8 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
     const int q = tid + i * kBlock;
     idv[i] = q < P ? p.ids[q] : -1;
   }
-  uint4 xv[MAXV];
-  load_slice<MAXV>(p, t, v0, v1, xv);
+  uint4 xv[MAXV][Unit<PAYLOAD>::kXV];
+  load_slice<PAYLOAD, MAXV>(p, t, u0, u1, xv);
 
   // two histograms: all ids, and ids at positions before this token's pairs
   // (s_a is cleared up to 64 whole chunks, so chunk reads see zeros past E)
@@ -330,10 +362,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   }
   row = checked_row(p, row);
   publish_rows(p, t, cc, row);
-  if (PAYLOAD == 0)
-    store_bf16<MAXV>(p, v0, v1, xv, row);
-  else
-    store_fp8<MAXV>(p, v0, v1, xv, row);
+  store_slice<PAYLOAD, MAXV>(p, u0, u1, xv, row);
 }
 
 // ---------------------------------------------------------------------------
@@ -430,12 +459,11 @@ template <int PAYLOAD, int MAXV>
 __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams p) {
   const int t = blockIdx.x / p.col_chunks;
   const int cc = blockIdx.x - t * p.col_chunks;
-  const int nvec = p.H / 8;
-  const int v0 = cc * p.vec_per_chunk;
-  const int v1 = min(v0 + p.vec_per_chunk, nvec);
+  const int u0 = cc * p.vec_per_chunk;
+  const int u1 = min(u0 + p.vec_per_chunk, units_per_row(p));
   const int lane = lane_id();
-  uint4 xv[MAXV];
-  load_slice<MAXV>(p, t, v0, v1, xv);
+  uint4 xv[MAXV][Unit<PAYLOAD>::kXV];
+  load_slice<PAYLOAD, MAXV>(p, t, u0, u1, xv);
   int row = -1;
   if (lane < p.k) {
     const int q = t * p.k + lane;
@@ -453,10 +481,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams
   }
   row = checked_row(p, row);
   publish_rows(p, t, cc, row);
-  if (PAYLOAD == 0)
-    store_bf16<MAXV>(p, v0, v1, xv, row);
-  else
-    store_fp8<MAXV>(p, v0, v1, xv, row);
+  store_slice<PAYLOAD, MAXV>(p, u0, u1, xv, row);
 }
 
 template <int PAYLOAD, int MAXV>
@@ -500,20 +525,21 @@ size_t dispatch_workspace_bytes(int T, int k, int E) {
 
 hipError_t launch_dispatch(const DispatchParams& in, hipStream_t st) {
   DispatchParams p = in;
-  const int nvec = p.H / 8;
+  const int nunits = units_per_row(p);
   const size_t P = (size_t)p.T * p.k;
-  // Column chunks, balanced, a multiple of 16 vectors so an fp8 scale block
-  // never straddles two blocks.  One vector per thread, except where the
-  // fused path's per-block recount of all T*k ids is heavy (T*k > 2048):
-  // there two vectors per thread halve the number of recounting blocks
-  // (measured: fp8 at T*k = 4096, 16.6 -> 15.0 us; no gain below).
+  // Column chunks of whole units (8 columns bf16, 16 fp8), balanced; a
+  // multiple of 128 columns, so an fp8 scale block never straddles two
+  // blocks.  One unit per thread, except where the fused path's per-block
+  // recount of all T*k ids is heavy (T*k > 2048): there two units per thread
+  // halve the number of recounting blocks.
   const bool wide = P > 2048 && P <= (size_t)kSmallMaxPairs;
   const int budget = wide ? 2 * kBlock : kBlock;
-  p.col_chunks = (nvec + budget - 1) / budget;
-  int vpc = (nvec + p.col_chunks - 1) / p.col_chunks;
-  vpc = (vpc + 15) / 16 * 16;
+  const int align = kFp8Block / (p.payload ? 16 : 8);
+  p.col_chunks = (nunits + budget - 1) / budget;
+  int vpc = (nunits + p.col_chunks - 1) / p.col_chunks;
+  vpc = (vpc + align - 1) / align * align;
   p.vec_per_chunk = vpc;
-  p.col_chunks = (nvec + vpc - 1) / vpc;
+  p.col_chunks = (nunits + vpc - 1) / vpc;
   p.nchunks = (int)((P + kChunkPairs - 1) / kChunkPairs);
   p.rows = p.C > 0 ? p.N * p.C : (int)P;
   if (P > (size_t)kSmallMaxPairs) {

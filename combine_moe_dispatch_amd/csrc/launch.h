@@ -34,7 +34,7 @@ struct DispatchParams {
   int payload;
   int nchunks;
   int col_chunks;     // blocks per token in the scatter
-  int vec_per_chunk;  // 16-byte source vectors per block
+  int vec_per_chunk;  // row units per block (8 columns bf16, 16 columns fp8)
 };
 
 size_t dispatch_workspace_bytes(int T, int k, int E);

@@ -157,3 +157,22 @@ def test_split_halves_reject_bad_arguments():
     assert r(ctypes.byref(s8), 16, None, ctypes.byref(lay), 16, None, 16, None) == 1  # scales
     assert c(ctypes.byref(s), 16, None, ctypes.byref(lay), None, None, None) == 1
     assert c(ctypes.byref(s8), 16, None, ctypes.byref(lay), 16, None, None) == 1
+
+
+def test_stream_floor_library_loads_and_rejects_bad_arguments():
+    """libmoe_ceiling.so (the benchmark's streaming floor kernels) loads, exports
+    its entry points, and refuses null or misaligned pointers and bad grids
+    without launching."""
+    path = os.path.join(os.path.dirname(api.LIB_PATH), "libmoe_ceiling.so")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.moe_ceiling_read.argtypes = [vp, sz, vp, i32, vp]
+    lib.moe_ceiling_write.argtypes = [vp, sz, i32, vp]
+    lib.moe_ceiling_copy.argtypes = [vp, vp, sz, i32, vp]
+    lib.moe_ceiling_empty.argtypes = [vp]
+    assert lib.moe_ceiling_read(None, 16, 256, 64, None) == 1
+    assert lib.moe_ceiling_read(4096, 16, None, 64, None) == 1
+    assert lib.moe_ceiling_read(4097, 16, 256, 64, None) == 1
+    assert lib.moe_ceiling_write(4096, 16, 0, None) == 1
+    assert lib.moe_ceiling_write(4096, 16, 70000, None) == 1
+    assert lib.moe_ceiling_copy(4096, 4104, 16, 64, None) == 1
