@@ -299,8 +299,7 @@ def run_gpu(args, w, inp):
 
 def payload_bytes(w):
     """Payload bytes one dispatch writes (and one combine reads): k rows per token."""
-    row = 2 * w.H if w.payload == "bf16" else w.H + 4 * (w.H // 128)
-    return w.tokens * w.k * row
+    return w.tokens * w.k * nbytes_row(w)
 
 
 def stream_floor(torch, stream, time_graph, nbytes, n):
