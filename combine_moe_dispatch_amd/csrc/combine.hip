@@ -26,41 +26,72 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// Fold n gathered rows into acc with fp32 fused multiply-adds in slot order.
+template <int N>
+__device__ __forceinline__ void fold_rows(float (&acc)[8], const uint4 (&yv)[N],
+                                          const int (&row)[N], const float (&wj)[N]) {
+#pragma unroll
+  for (int g = 0; g < N; ++g) {
+    if (row[g] < 0) continue;
+    const uint32_t q[4] = {yv[g].x, yv[g].y, yv[g].z, yv[g].w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc[2 * m] = fmaf(wj[g], bf16_lo(q[m]), acc[2 * m]);
+      acc[2 * m + 1] = fmaf(wj[g], bf16_hi(q[m]), acc[2 * m + 1]);
+    }
+  }
+}
+
+// K > 0: top-k fixed at compile time; the token's rows and weights are read
+// first, as wide uniform loads, before anything else waits.  K == 0: k at
+// run time, rows streamed kGroup at a time.  Grid: x = column chunk,
+// y = token.
+template <int K>
 __global__ void __launch_bounds__(kBlock)
 combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ token_row,
-                    const float* __restrict__ w, uint4* __restrict__ out, int H, int k,
-                    int col_chunks) {
-  const int t = blockIdx.x / col_chunks;
-  const int cc = blockIdx.x - t * col_chunks;
+                    const float* __restrict__ w, uint4* __restrict__ out, int H, int k_rt) {
+  const int k = K > 0 ? K : k_rt;
+  const int t = blockIdx.y;
   const int nvec = H / 8;
-  const int v = cc * kBlock + threadIdx.x;
+  const int v = blockIdx.x * kBlock + threadIdx.x;
   const int32_t* trow = token_row + (size_t)t * k;
   const float* tw = w + (size_t)t * k;
-  if (v >= nvec) return;
   float acc[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) acc[m] = 0.0f;
-  for (int j0 = 0; j0 < k; j0 += kGroup) {
-    int row[kGroup];
-    float wj[kGroup];
+  if constexpr (K > 0) {
+    int row[K];
+    float wj[K];
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      row[g] = j0 + g < k ? trow[j0 + g] : -1;
-      wj[g] = j0 + g < k ? tw[j0 + g] : 0.0f;
+    for (int g = 0; g < K; ++g) {
+      row[g] = trow[g];
+      wj[g] = tw[g];
     }
-    uint4 yv[kGroup];
+    // no early exit before the gathers: lanes past the row end only mask
+    // their accesses, so nothing delays the uniform loads above
+    const bool active = v < nvec;
+    uint4 yv[K];
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g)
-      yv[g] = row[g] >= 0 ? load_stream(&y[(size_t)row[g] * nvec + v]) : make_uint4(0, 0, 0, 0);
+    for (int g = 0; g < K; ++g)
+      yv[g] = active && row[g] >= 0 ? load_stream(&y[(size_t)row[g] * nvec + v])
+                                    : make_uint4(0, 0, 0, 0);
+    fold_rows<K>(acc, yv, row, wj);
+    if (!active) return;
+  } else {
+    if (v >= nvec) return;
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+      int row[kGroup];
+      float wj[kGroup];
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      if (row[g] < 0) continue;
-      const uint32_t q[4] = {yv[g].x, yv[g].y, yv[g].z, yv[g].w};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        acc[2 * m] = fmaf(wj[g], bf16_lo(q[m]), acc[2 * m]);
-        acc[2 * m + 1] = fmaf(wj[g], bf16_hi(q[m]), acc[2 * m + 1]);
+      for (int g = 0; g < kGroup; ++g) {
+        row[g] = j0 + g < k ? trow[j0 + g] : -1;
+        wj[g] = j0 + g < k ? tw[j0 + g] : 0.0f;
       }
+      uint4 yv[kGroup];
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g)
+        yv[g] = row[g] >= 0 ? load_stream(&y[(size_t)row[g] * nvec + v]) : make_uint4(0, 0, 0, 0);
+      fold_rows<kGroup>(acc, yv, row, wj);
     }
   }
   uint4 o;
@@ -145,11 +176,17 @@ hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_r
   const int per_block = payload == 0 ? kBlock : 2 * kBlock;  // vectors of 8 columns
   const int col_chunks = (H / 8 + per_block - 1) / per_block;
   const unsigned blocks = (unsigned)T * (unsigned)col_chunks;
-  if (payload == 0)
-    hipLaunchKernelGGL(combine_bf16_kernel, dim3(blocks), dim3(kBlock), 0, st,
-                       reinterpret_cast<const uint4*>(y), token_row, w,
-                       reinterpret_cast<uint4*>(out), H, k, col_chunks);
-  else
+  if (payload == 0) {
+    const dim3 grid((unsigned)col_chunks, (unsigned)T);
+    if (k == 8)
+      hipLaunchKernelGGL(combine_bf16_kernel<8>, grid, dim3(kBlock), 0, st,
+                         reinterpret_cast<const uint4*>(y), token_row, w,
+                         reinterpret_cast<uint4*>(out), H, k);
+    else
+      hipLaunchKernelGGL(combine_bf16_kernel<0>, grid, dim3(kBlock), 0, st,
+                         reinterpret_cast<const uint4*>(y), token_row, w,
+                         reinterpret_cast<uint4*>(out), H, k);
+  } else
     hipLaunchKernelGGL(combine_fp8_kernel, dim3(blocks), dim3(kBlock), 0, st,
                        reinterpret_cast<const uint2*>(y), ys, token_row, w,
                        reinterpret_cast<uint4*>(out), H, k, col_chunks);

@@ -99,6 +99,16 @@ __device__ __forceinline__ unsigned xcd_local_block(unsigned b, unsigned n) {
   return x * q + (x < r ? x : r) + b / kXcds;
 }
 
+// Block barrier that orders LDS accesses only.  __syncthreads() also waits
+// for every global load in flight (a workgroup fence covers global memory);
+// this one lets them stay in flight across the barrier.  Use it only where
+// no global memory written by one thread is read by another after it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Inclusive/exclusive sums over a wave64 with shuffles.
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
   const int lane = lane_id();

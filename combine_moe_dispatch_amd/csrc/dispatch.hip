@@ -45,7 +45,6 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / kWave;
-constexpr int kIdsPerThread = kSmallMaxPairs / kBlock;  // 16
 constexpr int kDevCapacity = 1;
 constexpr int kDevBadId = 2;
 
@@ -123,9 +122,9 @@ __device__ __forceinline__ void load_slice(const DispatchParams& p, int t, int u
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int u = u0 + threadIdx.x + i * kBlock;
+    const int uc = min(u, u1 - 1);  // clamped: units past u1 are loaded but never stored
 #pragma unroll
-    for (int c = 0; c < kXV; ++c)
-      xv[i][c] = u < u1 ? load_stream(&x[kXV * u + c]) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < kXV; ++c) xv[i][c] = load_stream(&x[kXV * uc + c]);
   }
 }
 
@@ -253,7 +252,11 @@ __device__ __forceinline__ int checked_row(const DispatchParams& p, int row) {
 // ---------------------------------------------------------------------------
 // Fused single-launch path.
 // ---------------------------------------------------------------------------
-template <int PAYLOAD, int MAXV>
+// IPT = ids per thread (T*k <= IPT * kBlock).  Every global load below is
+// unconditional (indices clamped into range, values masked afterwards), so
+// the compiler can count loads in flight exactly and wait only for the ids
+// before the histograms, not for the x slice issued after them.
+template <int PAYLOAD, int MAXV, int IPT>
 __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p) {
   __shared__ __align__(16) int s_a[kMaxExperts];  // histogram of all ids
   __shared__ int s_b[kMaxExperts + 1];  // block 0: scan; others: histogram before this token
@@ -265,17 +268,14 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   if (blockIdx.x == 0) {
     // histogram, scan and the global metadata; all id loads are issued
     // before the first one is used
-    int idv[kIdsPerThread];
+    int idv[IPT];
 #pragma unroll
-    for (int i = 0; i < kIdsPerThread; ++i) {
-      const int q = tid + i * kBlock;
-      idv[i] = q < P ? p.ids[q] : 0;
-    }
+    for (int i = 0; i < IPT; ++i) idv[i] = P > 0 ? p.ids[min(tid + i * kBlock, P - 1)] : 0;
     for (int e = tid; e < p.E; e += kBlock) s_a[e] = 0;
     __syncthreads();
     bool bad = false;
 #pragma unroll
-    for (int i = 0; i < kIdsPerThread; ++i) {
+    for (int i = 0; i < IPT; ++i) {
       if (tid + i * kBlock < P) {
         const int e = idv[i];
         if ((unsigned)e < (unsigned)p.E)
@@ -298,15 +298,13 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
 
   // issue every load first: this token's k ids, the whole id list (a few
   // per thread) and this block's slice of the token row
-  const int my_e = lane < p.k ? p.ids[t * p.k + lane] : -1;  // lane j: expert of slot j
-  int idv[kIdsPerThread];
+  const int my_e_raw = p.ids[t * p.k + min(lane, p.k - 1)];
+  int idv[IPT];
 #pragma unroll
-  for (int i = 0; i < kIdsPerThread; ++i) {
-    const int q = tid + i * kBlock;
-    idv[i] = q < P ? p.ids[q] : -1;
-  }
+  for (int i = 0; i < IPT; ++i) idv[i] = p.ids[min(tid + i * kBlock, P - 1)];
   uint4 xv[MAXV][Unit<PAYLOAD>::kXV];
   load_slice<PAYLOAD, MAXV>(p, t, u0, u1, xv);
+  const int my_e = lane < p.k ? my_e_raw : -1;  // lane j: expert of slot j
 
   // two histograms: all ids, and ids at positions before this token's pairs
   // (s_a is cleared up to 64 whole chunks, so chunk reads see zeros past E)
@@ -315,10 +313,12 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
     s_a[e] = 0;
     s_b[e] = 0;
   }
-  __syncthreads();
+  // LDS-only barriers from here on: the slice of x loaded above stays in
+  // flight while the histograms are built
+  lds_barrier();
   const int first_pos = t * p.k;
 #pragma unroll
-  for (int i = 0; i < kIdsPerThread; ++i) {
+  for (int i = 0; i < IPT; ++i) {
     const int q = tid + i * kBlock;
     if (q < P) {
       const int e = idv[i];
@@ -328,7 +328,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // Every wave on its own: lane l sums chunk l of csz consecutive experts, a
   // DPP scan turns the chunk sums into exclusive chunk prefixes, and lane j
@@ -484,13 +484,22 @@ __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams
   store_slice<PAYLOAD, MAXV>(p, u0, u1, xv, row);
 }
 
+static_assert(kSmallMaxPairs <= 16 * kBlock, "the fused path loads at most 16 ids per thread");
+
 template <int PAYLOAD, int MAXV>
 hipError_t launch_paths(const DispatchParams& p, hipStream_t st) {
   const long P = (long)p.T * p.k;
   if (P <= kSmallMaxPairs) {
     const unsigned blocks = 1u + (unsigned)p.T * (unsigned)p.col_chunks;
-    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV>), dim3(blocks), dim3(kBlock), 0,
-                       st, p);
+    if (P <= kBlock * 4)
+      hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 4>), dim3(blocks), dim3(kBlock), 0,
+                         st, p);
+    else if (P <= kBlock * 8)
+      hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 8>), dim3(blocks), dim3(kBlock), 0,
+                         st, p);
+    else
+      hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 16>), dim3(blocks), dim3(kBlock),
+                         0, st, p);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunks), dim3(kBlock), 0, st, p);
