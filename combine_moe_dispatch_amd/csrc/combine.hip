@@ -42,9 +42,9 @@ __device__ __forceinline__ void fold_rows(float (&acc)[8], const uint4 (&yv)[N],
   }
 }
 
-// K > 0: top-k fixed at compile time; the token's rows and weights are read
-// first, as wide uniform loads, before anything else waits.  K == 0: k at
-// run time, rows streamed kGroup at a time.  Grid: x = column chunk,
+// K > 0: top-k fixed at compile time, so the token's rows and weights are
+// read first, as wide uniform loads, before anything else waits; K == 0: k
+// at run time.  Rows are gathered kGroup at a time.  Grid: x = column chunk,
 // y = token.
 template <int K>
 __global__ void __launch_bounds__(kBlock)
@@ -56,44 +56,28 @@ combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ tok
   const int v = blockIdx.x * kBlock + threadIdx.x;
   const int32_t* trow = token_row + (size_t)t * k;
   const float* tw = w + (size_t)t * k;
+  // no early exit before the gathers: lanes past the row end only mask
+  // their accesses, so nothing delays the uniform loads of the token's rows
+  const bool active = v < nvec;
   float acc[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) acc[m] = 0.0f;
-  if constexpr (K > 0) {
-    int row[K];
-    float wj[K];
+  for (int j0 = 0; j0 < k; j0 += kGroup) {
+    int row[kGroup];
+    float wj[kGroup];
 #pragma unroll
-    for (int g = 0; g < K; ++g) {
-      row[g] = trow[g];
-      wj[g] = tw[g];
+    for (int g = 0; g < kGroup; ++g) {
+      row[g] = j0 + g < k ? trow[j0 + g] : -1;
+      wj[g] = j0 + g < k ? tw[j0 + g] : 0.0f;
     }
-    // no early exit before the gathers: lanes past the row end only mask
-    // their accesses, so nothing delays the uniform loads above
-    const bool active = v < nvec;
-    uint4 yv[K];
+    uint4 yv[kGroup];
 #pragma unroll
-    for (int g = 0; g < K; ++g)
+    for (int g = 0; g < kGroup; ++g)
       yv[g] = active && row[g] >= 0 ? load_stream(&y[(size_t)row[g] * nvec + v])
                                     : make_uint4(0, 0, 0, 0);
-    fold_rows<K>(acc, yv, row, wj);
-    if (!active) return;
-  } else {
-    if (v >= nvec) return;
-    for (int j0 = 0; j0 < k; j0 += kGroup) {
-      int row[kGroup];
-      float wj[kGroup];
-#pragma unroll
-      for (int g = 0; g < kGroup; ++g) {
-        row[g] = j0 + g < k ? trow[j0 + g] : -1;
-        wj[g] = j0 + g < k ? tw[j0 + g] : 0.0f;
-      }
-      uint4 yv[kGroup];
-#pragma unroll
-      for (int g = 0; g < kGroup; ++g)
-        yv[g] = row[g] >= 0 ? load_stream(&y[(size_t)row[g] * nvec + v]) : make_uint4(0, 0, 0, 0);
-      fold_rows<kGroup>(acc, yv, row, wj);
-    }
+    fold_rows<kGroup>(acc, yv, row, wj);
   }
+  if (!active) return;
   uint4 o;
   o.x = pack_bf16x2(acc[0], acc[1]);
   o.y = pack_bf16x2(acc[2], acc[3]);
@@ -108,10 +92,13 @@ combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ tok
 // partial lines: 1.67x the output bytes).  16 consecutive vectors share one
 // 128-column scale.  Workgroups are renumbered so that the column chunks of
 // one token run on one XCD and share the L2 lines of the token's scales.
+// K as for the bf16 kernel: K > 0 fixes top-k at compile time.
+template <int K>
 __global__ void __launch_bounds__(kBlock)
 combine_fp8_kernel(const uint2* __restrict__ y, const float* __restrict__ ys,
                    const int32_t* __restrict__ token_row, const float* __restrict__ w,
-                   uint4* __restrict__ out, int H, int k, int col_chunks) {
+                   uint4* __restrict__ out, int H, int k_rt, int col_chunks) {
+  const int k = K > 0 ? K : k_rt;
   const unsigned b = xcd_local_block(blockIdx.x, gridDim.x);
   const int t = b / col_chunks;
   const int cc = b - t * col_chunks;
@@ -121,7 +108,8 @@ combine_fp8_kernel(const uint2* __restrict__ y, const float* __restrict__ ys,
   const int u1 = u0 + kBlock;
   const int32_t* trow = token_row + (size_t)t * k;
   const float* tw = w + (size_t)t * k;
-  if (u0 >= nv) return;
+  // no early exit before the gathers (lanes past the row end mask them)
+  const bool has0 = u0 < nv;
   const bool has1 = u1 < nv;
   float acc[16];
 #pragma unroll
@@ -140,9 +128,9 @@ combine_fp8_kernel(const uint2* __restrict__ y, const float* __restrict__ ys,
     for (int g = 0; g < kGroup; ++g) {
       const bool on = row[g] >= 0;
       const size_t r = on ? (size_t)row[g] : 0;
-      c0[g] = on ? load_stream(&y[r * nv + u0]) : make_uint2(0, 0);
+      c0[g] = on && has0 ? load_stream(&y[r * nv + u0]) : make_uint2(0, 0);
       c1[g] = on && has1 ? load_stream(&y[r * nv + u1]) : make_uint2(0, 0);
-      s0[g] = on ? ys[r * nb + u0 / 16] : 0.0f;  // scales: cached loads
+      s0[g] = on && has0 ? ys[r * nb + u0 / 16] : 0.0f;  // scales: cached loads
       s1[g] = on && has1 ? ys[r * nb + u1 / 16] : 0.0f;
     }
 #pragma unroll
@@ -159,6 +147,7 @@ combine_fp8_kernel(const uint2* __restrict__ y, const float* __restrict__ ys,
       for (int m = 8; m < 16; ++m) acc[m] = fmaf(wj[g], dec[m] * s1[g], acc[m]);
     }
   }
+  if (!has0) return;
   uint4* o = out + (size_t)t * nv;
   store_stream(&o[u0], make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
@@ -187,9 +176,16 @@ hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_r
                          reinterpret_cast<const uint4*>(y), token_row, w,
                          reinterpret_cast<uint4*>(out), H, k);
   } else
-    hipLaunchKernelGGL(combine_fp8_kernel, dim3(blocks), dim3(kBlock), 0, st,
-                       reinterpret_cast<const uint2*>(y), ys, token_row, w,
-                       reinterpret_cast<uint4*>(out), H, k, col_chunks);
+  {
+    if (k == 8)
+      hipLaunchKernelGGL(combine_fp8_kernel<8>, dim3(blocks), dim3(kBlock), 0, st,
+                         reinterpret_cast<const uint2*>(y), ys, token_row, w,
+                         reinterpret_cast<uint4*>(out), H, k, col_chunks);
+    else
+      hipLaunchKernelGGL(combine_fp8_kernel<0>, dim3(blocks), dim3(kBlock), 0, st,
+                         reinterpret_cast<const uint2*>(y), ys, token_row, w,
+                         reinterpret_cast<uint4*>(out), H, k, col_chunks);
+  }
   return hipGetLastError();
 }
 

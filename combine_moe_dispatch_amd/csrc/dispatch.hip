@@ -462,14 +462,17 @@ __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams
   const int u0 = cc * p.vec_per_chunk;
   const int u1 = min(u0 + p.vec_per_chunk, units_per_row(p));
   const int lane = lane_id();
+  // the slot's id and in-chunk rank first (unconditional, clamped), then the
+  // x slice: the row's dependent loads wait only for the first two
+  const int q = t * p.k + min(lane, p.k - 1);
+  const int e = p.ids[q];
+  const int lr = p.local_rank[q];
   uint4 xv[MAXV][Unit<PAYLOAD>::kXV];
   load_slice<PAYLOAD, MAXV>(p, t, u0, u1, xv);
   int row = -1;
   if (lane < p.k) {
-    const int q = t * p.k + lane;
-    const int e = p.ids[q];
     if ((unsigned)e < (unsigned)p.E) {
-      const int pos = p.chunk_hist[(size_t)(q / kChunkPairs) * p.E + e] + p.local_rank[q];
+      const int pos = p.chunk_hist[(size_t)(q / kChunkPairs) * p.E + e] + lr;
       if (p.C > 0) {
         const int r = e / p.L;
         const int local = p.expert_offsets[e] - r * p.C + pos;
