@@ -210,6 +210,35 @@ def test_fp8_decode_all_codes_through_combine():
             assert got[c] == oracle.f32_to_bf16(v), (c, hex(got[c]))
 
 
+@pytest.mark.parametrize("T,k,payload_path", [(64, 8, "fused"), (600, 8, "chunked")])
+def test_fp8_quantiser_at_extreme_magnitudes(T, k, payload_path):
+    """Blocks of 128 columns scaled by powers of two from 2^-120 to 2^120 (bf16
+    subnormals included), all-zero blocks, and blocks whose small entries
+    fall far below the smallest e4m3 step next to one large entry: codes and
+    scales bit-exact against the oracle's IEEE division and encoder, on both
+    sides of the range where the kernel divides per element instead of
+    through the reciprocal."""
+    print(f"[case] fp8 extreme magnitudes T={T} k={k} ({payload_path})", flush=True)
+    H, E, N = 1408, 32, 4
+    C = T * min(k, E // N)
+    shape = api.Shape(T, H, E, k, N, C, api.MOE_PAYLOAD_FP8_E4M3_B128)
+    inp = inputs.generate(T, H, E, seed=4242)
+    x = inp.x_bits.view(np.uint16).astype(np.uint32) << 16
+    base = x.view(np.float32).reshape(T, H // 128, 128)
+    xf = base.copy()
+    exps = np.array([-120, -100, -90, -81, -79, -72, -70, -40, 0, 40, 70, 86, 88, 90, 100, 120])
+    e = exps[(np.arange(T)[:, None] * 5 + np.arange(H // 128)[None, :]) % len(exps)]
+    xf *= np.ldexp(np.float32(1), e)[:, :, None].astype(np.float32)
+    xf[::7, 3, :] = 0.0                     # all-zero blocks
+    xf[1::5, 5, :] = base[1::5, 5, :] * np.float32(2.0 ** -30)  # tiny entries beside one large one
+    xf[1::5, 5, 17] = np.float32(3.0)
+    xb = inputs.bf16_bits_from_f32(xf.reshape(T, H))
+    ids = inputs.random_ids(T, k, E, seed=4243)
+    w = inputs.random_weights(T, k, seed=4244)
+    g = run_chain(shape, xb, inp.alpha, ids=ids, weights=w)
+    check_chain(shape, g, xb, inp.alpha)
+
+
 @pytest.mark.parametrize("T,E,G,TG,k,zipf,ties", [
     (128, 256, 8, 4, 8, 0.0, False),   # DeepSeek-V3-style group routing
     (4096, 256, 8, 4, 8, 1.2, False),  # with a popularity bias
