@@ -87,43 +87,81 @@ __device__ __forceinline__ void store_partial(uint4* dst, const float* acc) {
                                      pack_bf16x2(acc[8 * h + 6], acc[8 * h + 7])));
 }
 
-// k <= kGroup: all k rows are loaded at once into registers, then each group
-// is folded (its slots in slot order) and stored in turn.  A lane owns KV
-// vectors of 8 columns, u and u + 64 (fp8: KV = 2, 8-byte code loads), so
-// every 16-byte store instruction of the wave covers 1 KB of a partial row
-// without gaps.  fp8 workgroups are renumbered so the column chunks of one
-// token share an XCD and the L2 lines of its scales.
-template <bool FP8>
+// k <= kGroup: the token's rows, ids and weights are wave-uniform, read with
+// scalar loads at the start (no vector load has to wait for them), and the
+// grouping by rank is scalar arithmetic.  All k rows are then gathered at
+// once into registers and each group is folded (its slots in slot order) and
+// stored in turn.  A lane owns KV vectors of 8 columns, u and u + 64 (fp8:
+// KV = 2, 8-byte code loads), so every 16-byte store instruction of the wave
+// covers 1 KB of a partial row without gaps.  fp8 workgroups are renumbered
+// so the column chunks of one token share an XCD and the L2 lines of its
+// scales.  K = 8 fixes k at compile time; K = 0 takes k <= 8 at run time.
+template <bool FP8, int K>
 __global__ void __launch_bounds__(kBlock)
 combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ ys,
                           const int32_t* __restrict__ token_row,
                           const int32_t* __restrict__ ids, const float* __restrict__ w,
                           uint4* __restrict__ partial, int32_t* __restrict__ partial_rank,
-                          int H, int k, int E, int L, int M, int col_chunks) {
+                          int H, int k_rt, int E, int L, int M, int col_chunks) {
   constexpr int KV = FP8 ? 2 : 1;
+  const int k = K > 0 ? K : k_rt;
   const unsigned b = FP8 ? xcd_local_block(blockIdx.x, gridDim.x) : blockIdx.x;
   const int t = b / col_chunks;
   const int cc = b - t * col_chunks;
   const int nv = H / 8;  // 8-column vectors per row
   const int nb = H / kFp8Block;
-  int u[KV];
-#pragma unroll
-  for (int i = 0; i < KV; ++i) u[i] = cc * kBlock * KV + (int)threadIdx.x + i * kBlock;
-  int my_row, my_group;
-  float my_w;
-  const int m = slot_groups(token_row, ids, w, partial_rank, t, cc, k, E, L, M, my_row, my_w,
-                            my_group);
-  // every slot's group, row and weight as wave-uniform values, read while
-  // all lanes are still active
-  int grp[kGroup], rj[kGroup];
+  const int lane = threadIdx.x;
+  // slot g: row, rank (-1 if skipped), weight -- uniform values
+  // (straight-line: every load is unconditional, slot indices clamped, so
+  // all of them are issued before the first wait)
+  int rj[kGroup], ej[kGroup], rank[kGroup];
   float wj[kGroup];
 #pragma unroll
   for (int g = 0; g < kGroup; ++g) {
-    grp[g] = g < k ? __builtin_amdgcn_readlane(my_group, g) : -1;
-    rj[g] = g < k ? __builtin_amdgcn_readlane(my_row, g) : -1;
-    wj[g] = g < k ? readlane_f(my_w, g) : 0.0f;
+    const size_t q = (size_t)t * k + min(g, k - 1);
+    rj[g] = token_row[q];
+    ej[g] = ids[q];
+    wj[g] = w[q];
   }
-  if (u[0] >= nv) return;
+#pragma unroll
+  for (int g = 0; g < kGroup; ++g) {
+    const bool ok = (g < k) & (rj[g] >= 0) & ((unsigned)ej[g] < (unsigned)E);
+    const int rk = max(ej[g], 0) / L;
+    rank[g] = ok ? rk : -1;
+    rj[g] = g < k ? rj[g] : -1;
+    wj[g] = g < k ? wj[g] : 0.0f;
+  }
+  // group of slot g = index of its rank among the token's distinct ranks in
+  // ascending order; m = number of distinct ranks
+  bool first[kGroup];  // slot g is the first slot of its rank
+  int grp[kGroup];
+  int m = 0;
+#pragma unroll
+  for (int g = 0; g < kGroup; ++g) {
+    bool f = rank[g] >= 0;
+#pragma unroll
+    for (int g2 = 0; g2 < g; ++g2) f = f & (rank[g2] != rank[g]);
+    first[g] = f;
+    m += f ? 1 : 0;
+  }
+#pragma unroll
+  for (int g = 0; g < kGroup; ++g) {
+    int below = 0;  // distinct ranks smaller than rank[g]
+#pragma unroll
+    for (int g2 = 0; g2 < kGroup; ++g2) below += (first[g2] & (rank[g2] < rank[g])) ? 1 : 0;
+    grp[g] = rank[g] >= 0 ? below : -1;
+  }
+  if (cc == 0 && lane < M) {
+    int r = -1;
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) r = grp[g] == lane ? rank[g] : r;
+    partial_rank[(size_t)t * M + lane] = r;
+  }
+  int u[KV];
+#pragma unroll
+  for (int i = 0; i < KV; ++i) u[i] = cc * kBlock * KV + lane + i * kBlock;
+  // no early exit before the gathers: lanes past the row end mask them
+  const bool active = u[0] < nv;
   // raw loads of every slot's vectors; each is decoded once, in its group
   uint4 yv[kGroup];      // bf16: 8 values
   uint2 cv[kGroup][KV];  // fp8: 8 codes per vector
@@ -143,8 +181,10 @@ combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ 
     const uint4* y16 = reinterpret_cast<const uint4*>(y);
 #pragma unroll
     for (int g = 0; g < kGroup; ++g)
-      yv[g] = grp[g] >= 0 ? load_stream(&y16[(size_t)rj[g] * nv + u[0]]) : make_uint4(0, 0, 0, 0);
+      yv[g] = active && grp[g] >= 0 ? load_stream(&y16[(size_t)rj[g] * nv + u[0]])
+                                    : make_uint4(0, 0, 0, 0);
   }
+  if (!active) return;
   for (int q = 0; q < m; ++q) {
     float acc[8 * KV];
 #pragma unroll
@@ -309,14 +349,16 @@ hipError_t launch_combine_send(const void* y, const float* ys, const int32_t* to
     // 64 vectors of 8 columns per block (bf16), 128 (fp8)
     const int chunks = (H / 8 + kBlock * (payload ? 2 : 1) - 1) / (kBlock * (payload ? 2 : 1));
     const unsigned nblk = (unsigned)T * (unsigned)chunks;
-    if (payload == 0)
-      hipLaunchKernelGGL((combine_send_small_kernel<false>), dim3(nblk), dim3(kBlock), 0, st, y,
-                         ys, token_row, ids, w, reinterpret_cast<uint4*>(partial), partial_rank,
-                         H, k, E, L, M, chunks);
-    else
-      hipLaunchKernelGGL((combine_send_small_kernel<true>), dim3(nblk), dim3(kBlock), 0, st, y,
-                         ys, token_row, ids, w, reinterpret_cast<uint4*>(partial), partial_rank,
-                         H, k, E, L, M, chunks);
+#define MOE_SEND_SMALL(FP8, K)                                                              \
+  hipLaunchKernelGGL((combine_send_small_kernel<FP8, K>), dim3(nblk), dim3(kBlock), 0, st, y, \
+                     ys, token_row, ids, w, reinterpret_cast<uint4*>(partial), partial_rank,  \
+                     H, k, E, L, M, chunks)
+    if (payload == 0) {
+      if (k == kGroup) MOE_SEND_SMALL(false, kGroup); else MOE_SEND_SMALL(false, 0);
+    } else {
+      if (k == kGroup) MOE_SEND_SMALL(true, kGroup); else MOE_SEND_SMALL(true, 0);
+    }
+#undef MOE_SEND_SMALL
     return hipGetLastError();
   }
   if (payload == 0)
