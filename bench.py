@@ -393,8 +393,20 @@ def cpu_baseline(w, inp, seconds):
             "sample": f"{reps} full {w.name} steps (oracle dispatch + double-precision combine, "
                       f"C, one thread); {1e6 * td / reps:.0f} us dispatch + "
                       f"{1e6 * tc / reps:.0f} us combine per step",
-            "host": platform.processor() or platform.machine(),
+            "host": cpu_model(),
             "nproc": os.cpu_count()}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo where there is one)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def main():
