@@ -133,17 +133,7 @@ __device__ __forceinline__ int wave_inclusive_sum_dpp(int x) {
   return x;
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
-}
 
-__device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
-}
 
 // Lanes of this wave whose `key` equals this lane's key (a 64-bit mask),
 // built one key bit at a time from ballots.  `bits` = number of key bits.

@@ -73,6 +73,20 @@ __device__ __forceinline__ void top2_take(float l, float& m1, float& m2) {
   m1 = above1 ? l : m1;
 }
 
+// Sum of s over lanes 0..31 (all other lanes hold 0), the same value in
+// every lane: a DPP row-shift inclusive sum inside each 16-lane row, then the
+// totals of rows 0 and 1 read with readlane.
+__device__ __forceinline__ float slot_sum(float s) {
+  float x = s;
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+  return r0 + r1;
+}
+
 // LDS hand-off inside one wavefront (no block barrier: waves exit early).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -92,20 +106,25 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
 
-  float v[VPL];
+  // every load is unconditional (index clamped, value masked below) and all
+  // are issued before the first is used: one memory round trip
+  float v[VPL], bv_[VPL];
   int id[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) v[i] = row[min(i * kWave + lane, E - 1)];
+  if (bias) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) bv_[i] = bias[min(i * kWave + lane, E - 1)];
+  } else {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) bv_[i] = 0.0f;
+  }
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = i * kWave + lane;
-    if (e < E) {
-      float l = row[e];
-      if (bias) l = l + bias[e];
-      v[i] = l;
-      id[i] = e;
-    } else {
-      v[i] = -INFINITY;
-      id[i] = kNone;
-    }
+    const bool in = e < E;
+    v[i] = in ? (bias ? v[i] + bv_[i] : v[i]) : -INFINITY;
+    id[i] = in ? e : kNone;
   }
   if (GROUPED) {
     float* sl = s_logit[wave];
@@ -200,14 +219,16 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
   }
 
   float s = 0.0f;
-  const float top = __shfl(my_val, 0, kWave);
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
   if (lane < k) {
     if (score == 1)
       s = 1.0f / (1.0f + expf(-my_val));
     else
       s = expf(my_val - top);
   }
-  const float sum = wave_sum_f(s);
+  // sum over lanes 0..k-1 (k <= 32: rows 0 and 1) in slot order within each
+  // DPP row, then the two row sums
+  const float sum = slot_sum(s);
   if (lane < k) {
     ids[(size_t)t * k + lane] = my_id;
     weights[(size_t)t * k + lane] = s / sum;
