@@ -296,30 +296,35 @@ combine_send_kernel(const uint4* __restrict__ y, const float* __restrict__ ys,
   }
 }
 
+// MM > 0: M (partial slots per token) fixed at compile time, so the slot
+// ranks are one wide uniform load issued with the kernel arguments; MM == 0:
+// M at run time.  No lane exits before the gathers.
+template <int MM>
 __global__ void __launch_bounds__(kBlock)
 combine_recv_kernel(const uint4* __restrict__ partial, const int32_t* __restrict__ partial_rank,
-                    uint4* __restrict__ out, int H, int M, int col_chunks) {
+                    uint4* __restrict__ out, int H, int M_rt, int col_chunks) {
+  const int M = MM > 0 ? MM : M_rt;
   const int t = blockIdx.x / col_chunks;
   const int cc = blockIdx.x - t * col_chunks;
   const int nvec = H / 8;
   const int v = cc * kBlock + threadIdx.x;
-  if (v >= nvec) return;
+  const bool active = v < nvec;
   const int32_t* pr = partial_rank + (size_t)t * M;
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
   for (int i0 = 0; i0 < M; i0 += kGroup) {
+    bool used[kGroup];
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) used[g] = i0 + g < M && pr[i0 + g] >= 0;
     uint4 pv[kGroup];
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      const int i = i0 + g;
-      pv[g] = (i < M && pr[i] >= 0) ? load_stream(&partial[((size_t)t * M + i) * nvec + v])
-                                    : make_uint4(0, 0, 0, 0);
-    }
+    for (int g = 0; g < kGroup; ++g)
+      pv[g] = active && used[g] ? load_stream(&partial[((size_t)t * M + i0 + g) * nvec + v])
+                                : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
-      const int i = i0 + g;
-      if (i >= M || pr[i] < 0) continue;
+      if (!used[g]) continue;
       const uint32_t q4[4] = {pv[g].x, pv[g].y, pv[g].z, pv[g].w};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -328,6 +333,7 @@ combine_recv_kernel(const uint4* __restrict__ partial, const int32_t* __restrict
       }
     }
   }
+  if (!active) return;
   store_stream(&out[(size_t)t * nvec + v],
                make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                           pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
@@ -379,9 +385,15 @@ hipError_t launch_combine_recv(const void* partial, const int32_t* partial_rank,
   if (T == 0) return hipSuccess;
   const int nvec = H / 8;
   const int col_chunks = (nvec + kBlock - 1) / kBlock;
-  hipLaunchKernelGGL(combine_recv_kernel, dim3((unsigned)T * (unsigned)col_chunks), dim3(kBlock),
-                     0, st, reinterpret_cast<const uint4*>(partial), partial_rank,
-                     reinterpret_cast<uint4*>(out), H, M, col_chunks);
+  const dim3 grid((unsigned)T * (unsigned)col_chunks);
+  if (M == kGroup)
+    hipLaunchKernelGGL(combine_recv_kernel<kGroup>, grid, dim3(kBlock), 0, st,
+                       reinterpret_cast<const uint4*>(partial), partial_rank,
+                       reinterpret_cast<uint4*>(out), H, M, col_chunks);
+  else
+    hipLaunchKernelGGL(combine_recv_kernel<0>, grid, dim3(kBlock), 0, st,
+                       reinterpret_cast<const uint4*>(partial), partial_rank,
+                       reinterpret_cast<uint4*>(out), H, M, col_chunks);
   return hipGetLastError();
 }
 

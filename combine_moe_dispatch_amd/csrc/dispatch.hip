@@ -485,24 +485,28 @@ __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams
   const int u0 = cc * p.vec_per_chunk;
   const int u1 = min(u0 + p.vec_per_chunk, units_per_row(p));
   const int lane = lane_id();
-  // the slot's id and in-chunk rank first (unconditional, clamped), then the
-  // x slice: the row's dependent loads wait only for the first two
+  // Loads in dependency order, all unconditional (indices clamped, values
+  // masked), so each wait covers only what it needs: the slot's id and
+  // in-chunk rank; then, from the id, the chunk base and the expert offset;
+  // then the x slice, which stays in flight while the row is formed.
   const int q = t * p.k + min(lane, p.k - 1);
   const int e = p.ids[q];
   const int lr = p.local_rank[q];
+  const bool valid = lane < p.k && (unsigned)e < (unsigned)p.E;
+  const int ec = valid ? e : 0;
+  const int base = p.chunk_hist[(size_t)(q / kChunkPairs) * p.E + ec];
+  const int eoff = p.expert_offsets[ec];
   uint4 xv[MAXV][Unit<PAYLOAD>::kXV];
   load_slice<PAYLOAD, MAXV>(p, t, u0, u1, xv);
   int row = -1;
-  if (lane < p.k) {
-    if ((unsigned)e < (unsigned)p.E) {
-      const int pos = p.chunk_hist[(size_t)(q / kChunkPairs) * p.E + e] + lr;
-      if (p.C > 0) {
-        const int r = e / p.L;
-        const int local = p.expert_offsets[e] - r * p.C + pos;
-        if (local < p.C) row = r * p.C + local;
-      } else {
-        row = p.expert_offsets[e] + pos;
-      }
+  if (valid) {
+    const int pos = base + lr;
+    if (p.C > 0) {
+      const int r = e / p.L;
+      const int local = eoff - r * p.C + pos;
+      if (local < p.C) row = r * p.C + local;
+    } else {
+      row = eoff + pos;
     }
   }
   row = checked_row(p, row);
