@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true")
+    ap.add_argument("--split", action="store_true",
+                    help="also time the receive-side shuffle into dense grouped-GEMM rows "
+                         "(moe_dispatch_recv) and its inverse (moe_combine_send)")
     ap.add_argument("--no-floor", action="store_true",
                     help="skip the streaming read/write floor at the payload size")
     ap.add_argument("--groups", type=int, default=1,
@@ -89,7 +92,7 @@ def nbytes_row(w):
 # a PMC figure stays valid while these are unchanged.
 KERNEL_SOURCES = {
     "route": ["route_topk.hip"],
-    "dispatch": ["dispatch.hip", "sources.hip"],
+    "dispatch": ["dispatch.hip", "sources.hip", "gemm_io.hip"],
     "combine": ["combine.hip", "combine_partial.hip"],
 }
 SHARED_SOURCES = ["device_common.h", "launch.h", "capi.hip"]
@@ -112,6 +115,8 @@ def profile_tag(args):
         tag += "_two_stage"
     if args.groups > 1:
         tag += "_grouped"
+    if args.split:
+        tag += "_split"
     return tag
 
 
@@ -147,7 +152,7 @@ def copy_calibration():
 
 
 class BufferSet:
-    def __init__(self, api, w, shape, inp, torch, np, two_stage=False):
+    def __init__(self, api, w, shape, inp, torch, np, two_stage=False, split=False):
         dev = "cuda"
         self.logits = torch.from_numpy(inp.logits).to(dev)
         self.bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
@@ -165,6 +170,12 @@ class BufferSet:
         M = api.partial_slots(shape) if two_stage else 0
         self.partial = torch.empty(w.tokens, M, w.H, dtype=torch.int16, device=dev)
         self.prank = torch.empty(w.tokens, M, dtype=torch.int32, device=dev)
+        if split:  # dense grouped-GEMM rows, and regions the send half writes back into
+            dense = api.Shape(shape.num_tokens, shape.hidden, shape.num_experts, shape.top_k,
+                              shape.num_ranks, 0, shape.payload)
+            self.gx, self.gs = api.alloc_recv(dense, dev)
+            self.goff = torch.empty(w.E + 1, dtype=torch.int32, device=dev)
+            self.ey, self.eys = api.alloc_recv(shape, dev)
 
 
 def run_gpu(args, w, inp):
@@ -181,7 +192,7 @@ def run_gpu(args, w, inp):
     nbytes = algorithmic_bytes(w)
     per_step = nbytes["dispatch"] + nbytes["combine"] + nbytes["route"]
     S = args.sets or min(64, max(2, math.ceil(2 * MALL_BYTES / per_step)))
-    sets = [BufferSet(api, w, shape, inp, torch, np, args.combine == "two-stage")
+    sets = [BufferSet(api, w, shape, inp, torch, np, args.combine == "two-stage", args.split)
             for _ in range(S)]
     stream = torch.cuda.Stream()
 
@@ -220,6 +231,12 @@ def run_gpu(args, w, inp):
         dispatch(s)
         combine(s)
 
+    def dispatch_recv(s):  # receive regions -> dense grouped-GEMM input
+        api.moe_dispatch_recv(shape, s.recv, s.rs, s.lay, s.gx, s.gs, s.goff, stream=stream)
+
+    def combine_send_back(s):  # dense rows -> receive-region layout
+        api.moe_combine_send(shape, s.gx, s.gs, s.lay, s.ey, s.eys, stream=stream)
+
     with torch.cuda.stream(stream):
         for s in sets:   # layout + expert outputs for every set (untimed)
             route(s)
@@ -229,6 +246,7 @@ def run_gpu(args, w, inp):
     stream.synchronize()
     status = int(sets[0].lay.status.item())
     partial_rows = int((sets[0].prank >= 0).sum().item()) if two_stage else 0
+    placed_rows = int((sets[0].lay.token_row >= 0).sum().item())
 
     def capture(fn_list, n, rotate):
         g = torch.cuda.CUDAGraph()
@@ -257,7 +275,7 @@ def run_gpu(args, w, inp):
         return sorted(ts)[len(ts) // 2]
 
     K, W = args.steps, args.warmup
-    res = {"sets": S, "status": status, "partial_rows": partial_rows}
+    res = {"sets": S, "status": status, "partial_rows": partial_rows, "placed_rows": placed_rows}
     for mode, rotate in (("cold", True), ("warm", False)):
         if mode == "warm" and args.no_warm:
             continue
@@ -290,6 +308,15 @@ def run_gpu(args, w, inp):
             r["combine_send_us"] = time_graph(g_send, K, reps=3)
             r["combine_recv_us"] = time_graph(g_recv, K, reps=3)
             del g_send, g_recv
+        if args.split:
+            g_dr = capture([dispatch_recv], K, rotate)
+            g_cs = capture([combine_send_back], K, rotate)
+            with torch.cuda.stream(stream):
+                g_dr.replay()
+                g_cs.replay()
+            r["dispatch_recv_us"] = time_graph(g_dr, K, reps=3)
+            r["combine_send_back_us"] = time_graph(g_cs, K, reps=3)
+            del g_dr, g_cs
         res[mode] = r
         del g_step, g_route, g_disp, g_comb
     if not args.no_floor:
@@ -483,6 +510,16 @@ def main():
         line["two_stage_combine"] = {
             "send_us": round(cold["combine_send_us"], 3), "recv_us": round(cold["combine_recv_us"], 3),
             "partial_rows": g["partial_rows"], "rows_per_token": round(g["partial_rows"] / w.tokens, 3)}
+    if "dispatch_recv_us" in cold:
+        # each placed row is read once and written once, plus (counts, offsets) per expert
+        # read and the dense offsets written
+        moved = 2 * g["placed_rows"] * nbytes_row(w) + 8 * w.E + 4 * (w.E + 1)
+        line["split"] = {
+            "dispatch_recv_us": round(cold["dispatch_recv_us"], 3),
+            "combine_send_us": round(cold["combine_send_back_us"], 3),
+            "bytes_each": moved,
+            "dispatch_recv_GBps": round(moved / (cold["dispatch_recv_us"] * 1e-6) / 1e9, 1),
+            "combine_send_GBps": round(moved / (cold["combine_send_back_us"] * 1e-6) / 1e9, 1)}
     if "warm" in g:
         wm = g["warm"]
         wus = wm["dispatch_us"] + wm["combine_us"]

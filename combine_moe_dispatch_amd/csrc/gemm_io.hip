@@ -14,8 +14,9 @@
 //
 // Each block rebuilds dense[] in LDS (placed count per expert, then a scan),
 // block 0 publishes it, and the block moves kRows dense rows: a binary search
-// in LDS finds a row's expert, and the row moves as 16-byte streaming
-// accesses (fp8 rows carry their H/128 scales along).
+// in LDS finds a row's expert, and the rows move as 16-byte streaming
+// accesses, every load of a pass issued before its stores (fp8 rows carry
+// their H/128 scales along).
 #include "device_common.h"
 #include "launch.h"
 
@@ -28,10 +29,18 @@ constexpr int kRows = 4;  // dense rows per block
 
 // dense[0..E]: exclusive scan of the placed rows per expert (a segment may be
 // cut short by its rank's capacity).
+// Also copies the segment offsets into off[0..E).
 __device__ void dense_offsets(const int32_t* counts, const int32_t* offsets, int E, int L, int C,
-                              int* dense, int* wave_tot) {
+                              int* dense, int* off, int* wave_tot) {
   const int per = (E + kBlock - 1) / kBlock;  // <= 4
   const int start = threadIdx.x * per;
+  int cnt[4], o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // all loads first (clamped), one round trip
+    const int e = min(start + i, E - 1);
+    cnt[i] = counts[e];
+    o[i] = offsets[e];
+  }
   int placed[4];
   int local = 0;
 #pragma unroll
@@ -39,8 +48,9 @@ __device__ void dense_offsets(const int32_t* counts, const int32_t* offsets, int
     const int e = start + i;
     int p = 0;
     if (i < per && e < E) {
-      p = counts[e];
-      if (C > 0) p = max(0, min(p, (e / L) * C + C - offsets[e]));
+      p = cnt[i];
+      if (C > 0) p = max(0, min(p, (e / L) * C + C - o[i]));
+      off[e] = o[i];
     }
     placed[i] = p;
     local += p;
@@ -79,7 +89,11 @@ __device__ __forceinline__ int find_expert(const int* dense, int E, int i) {
   return lo;
 }
 
-// PACK: receive regions -> dense rows; otherwise dense rows -> regions.
+constexpr int kVecsPerThread = 4;  // 16-byte vectors of one row per thread and pass
+
+// PACK: receive regions -> dense rows; otherwise dense rows -> regions.  The
+// block's kRows rows are located first (binary search in LDS), then each pass
+// issues every load of those rows before the first store.
 template <bool PACK>
 __global__ void __launch_bounds__(kBlock)
 gemm_io_kernel(const uint8_t* __restrict__ src, const float* __restrict__ src_scales,
@@ -87,25 +101,55 @@ gemm_io_kernel(const uint8_t* __restrict__ src, const float* __restrict__ src_sc
                const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
                int32_t* __restrict__ dense_out, int E, int L, int C, int row_bytes, int nb) {
   __shared__ int s_dense[kMaxExperts + 1];
+  __shared__ int s_off[kMaxExperts];
   __shared__ int s_wave[kBlock / kWave];
-  dense_offsets(counts, offsets, E, L, C, s_dense, s_wave);
+  dense_offsets(counts, offsets, E, L, C, s_dense, s_off, s_wave);
   if (PACK && blockIdx.x == 0)
     for (int e = threadIdx.x; e <= E; e += kBlock) dense_out[e] = s_dense[e];
   const int total = s_dense[E];
   const int nvec = row_bytes / 16;
+  bool ok[kRows];
+  size_t from[kRows], to[kRows];
+#pragma unroll
   for (int r = 0; r < kRows; ++r) {
     const int i = blockIdx.x * kRows + r;
-    if (i >= total) break;  // uniform
-    const int e = find_expert(s_dense, E, i);
-    const int region_row = offsets[e] + (i - s_dense[e]);
-    const size_t from = PACK ? (size_t)region_row : (size_t)i;
-    const size_t to = PACK ? (size_t)i : (size_t)region_row;
-    const uint4* s4 = reinterpret_cast<const uint4*>(src + from * row_bytes);
-    uint4* d4 = reinterpret_cast<uint4*>(dst + to * row_bytes);
-    for (int v = threadIdx.x; v < nvec; v += kBlock) store_stream(&d4[v], load_stream(&s4[v]));
-    if (src_scales)
-      for (int b = threadIdx.x; b < nb; b += kBlock)
-        store_stream(&dst_scales[to * nb + b], load_stream(&src_scales[from * nb + b]));
+    ok[r] = i < total;  // uniform
+    const int e = ok[r] ? find_expert(s_dense, E, i) : 0;
+    const size_t region_row = (size_t)(s_off[e] + (i - s_dense[e]));
+    from[r] = PACK ? region_row : (size_t)i;
+    to[r] = PACK ? (size_t)i : region_row;
+  }
+  for (int v0 = 0; v0 < nvec; v0 += kVecsPerThread * kBlock) {
+    uint4 buf[kRows][kVecsPerThread];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const uint4* s4 = reinterpret_cast<const uint4*>(src + from[r] * row_bytes);
+#pragma unroll
+      for (int j = 0; j < kVecsPerThread; ++j) {
+        const int v = v0 + j * kBlock + threadIdx.x;
+        buf[r][j] = ok[r] && v < nvec ? load_stream(&s4[v]) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      uint4* d4 = reinterpret_cast<uint4*>(dst + to[r] * row_bytes);
+#pragma unroll
+      for (int j = 0; j < kVecsPerThread; ++j) {
+        const int v = v0 + j * kBlock + threadIdx.x;
+        if (ok[r] && v < nvec) store_stream(&d4[v], buf[r][j]);
+      }
+    }
+  }
+  if (src_scales) {
+    for (int b0 = 0; b0 < nb; b0 += kBlock) {
+      float sc[kRows];
+      const int b = b0 + threadIdx.x;
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) sc[r] = ok[r] && b < nb ? src_scales[from[r] * nb + b] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < kRows; ++r)
+        if (ok[r] && b < nb) dst_scales[to[r] * nb + b] = sc[r];
+    }
   }
 }
 
