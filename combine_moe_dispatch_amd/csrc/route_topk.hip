@@ -8,8 +8,8 @@
 // Each lane holds ceil(E/64) biased logits (coalesced: value i of lane l is
 // expert i*64 + l) and sorts them once, best first, by (value descending, id
 // ascending).  Each of the k rounds then takes every lane's head, finds the
-// wave's best (value, id) with a DPP butterfly inside each 16-lane row and
-// four readlanes across the rows, and the owning lane pops its head.  Equal
+// wave's best (value, id) with a DPP butterfly inside each 16-lane row and two
+// DPP row broadcasts across the rows, and the owning lane pops its head.  Equal
 // values go to the lower expert id, so slots come out in descending order.
 // Lanes 0..k-1 then form the weights in fp32 and normalise them to one.
 //
@@ -44,25 +44,33 @@ __device__ __forceinline__ void dpp_max_step(float& v, int& i) {
   }
 }
 
-// Best (value, id) over the wave; the result is uniform.
+// The same with a row mask: rows outside ROWMASK keep their own pair.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ void dpp_max_step_rows(float& v, int& i) {
+  const float ov = __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWMASK, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROWMASK, 0xf, false);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// Best (value, id) over the wave; the result is uniform.  Four butterfly
+// steps leave every lane of a 16-lane row with the row's best; the row
+// broadcasts then fold row 0 into row 1 and row 2 into row 3 (lane 15 of the
+// row before), and row 1 into rows 2-3 (lane 31), so lane 63 holds the wave's
+// best.  (better() is a strict order on distinct ids, so the order of folding
+// does not matter.)
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   dpp_max_step<0xB1>(v, i);   // quad_perm [1,0,3,2]: lane ^ 1
   dpp_max_step<0x4E>(v, i);   // quad_perm [2,3,0,1]: lane ^ 2
   dpp_max_step<0x141>(v, i);  // row_half_mirror: quad <-> neighbouring quad
   dpp_max_step<0x140>(v, i);  // row_mirror: half-row <-> other half-row
-  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) {
-    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
-    const int ri = __builtin_amdgcn_readlane(i, 16 * r);
-    if (better(rv, ri, bv, bi)) {
-      bv = rv;
-      bi = ri;
-    }
-  }
-  v = bv;
-  i = bi;
+  dpp_max_step_rows<0x142, 0xa>(v, i);  // row_bcast:15 into rows 1 and 3
+  dpp_max_step_rows<0x143, 0xc>(v, i);  // row_bcast:31 into rows 2 and 3
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
 }
 
 // Keep the two largest values seen (equal values fill both).
