@@ -21,10 +21,12 @@
 //  * fused (T*k <= kSmallMaxPairs): one launch.  Block 0 builds the global
 //    histogram and scan and writes the metadata; every other block owns one
 //    (token, column chunk).  It loads the whole id list (a few ids per
-//    thread) and its slice of the token row at once, builds two LDS
-//    histograms (all ids; ids before this token); then each wave scans 64
-//    chunk sums of the first with DPP, reads its k rows off them into lanes
-//    0..k-1, and stores its slice of the row k times.
+//    thread) and its slice of the token row at once, and builds one LDS
+//    histogram holding two counts per expert (all ids; ids before this
+//    token).  Lanes 0..k-1 then form their slots' rows: with fixed-capacity
+//    regions of few experts per rank, from a direct sum over the rank's
+//    counts; otherwise from a DPP scan of 64 chunk sums in every wave.  The
+//    block stores its slice of the row k times.
 //  * chunked (larger T*k): (1) per chunk of 1024 pairs, a block computes each
 //    pair's rank among equal experts inside the chunk (wave ballot matching,
 //    no atomics on the placement path) and the chunk's histogram; (2) one
@@ -268,6 +270,37 @@ __device__ __forceinline__ int chunk_sum_below(const int* hist, int ci, int csz,
   return s;
 }
 
+// Rank of expert e (e / L) without a division: e and L are below 2^10 here,
+// so the rounded-up reciprocal is exact (e * L < 2^32).
+__device__ __forceinline__ int rank_of(const DispatchParams& p, int e) {
+  return p.L == 1 ? e : (int)__umulhi((uint32_t)e, p.l_magic);
+}
+
+// Ranks of at most this many experts take the direct in-rank prefix.
+constexpr int kDirectMaxL = 32;
+
+// Sum of hist[first .. e), first = the rank's first expert, e inside the rank
+// (e < first + L <= first + kDirectMaxL).  With L % 4 == 0 the rank's counts
+// are read as whole 16-byte vectors, all issued before the first is used.
+__device__ __forceinline__ int rank_prefix(const int* hist, int first, int e, int L) {
+  int s = 0;
+  if ((L & 3) == 0) {
+    const int4* h4 = reinterpret_cast<const int4*>(hist + first);
+    int4 q[kDirectMaxL / 4];
+#pragma unroll
+    for (int c = 0; c < kDirectMaxL / 4; ++c) q[c] = 4 * c < L ? h4[c] : make_int4(0, 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < kDirectMaxL / 4; ++c) {
+      const int x = first + 4 * c;
+      s += (x + 0 < e ? q[c].x : 0) + (x + 1 < e ? q[c].y : 0) + (x + 2 < e ? q[c].z : 0) +
+           (x + 3 < e ? q[c].w : 0);
+    }
+  } else {
+    for (int x = first; x < e; ++x) s += hist[x];
+  }
+  return s;
+}
+
 __device__ __forceinline__ int checked_row(const DispatchParams& p, int row) {
   return (row >= 0 && row < p.rows) ? row : -1;
 }
@@ -281,8 +314,8 @@ __device__ __forceinline__ int checked_row(const DispatchParams& p, int row) {
 // before the histograms, not for the x slice issued after them.
 template <int PAYLOAD, int MAXV, int IPT>
 __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p) {
-  __shared__ __align__(16) int s_a[kMaxExperts];  // histogram of all ids
-  __shared__ int s_b[kMaxExperts + 1];  // block 0: scan; others: histogram before this token
+  __shared__ __align__(16) int s_a[kMaxExperts];  // histogram (packed pair in the scatter blocks)
+  __shared__ int s_b[kMaxExperts + 1];  // block 0: its exclusive scan
   __shared__ int s_wave[kWaves];
   const int P = p.T * p.k;
   const int tid = threadIdx.x;
@@ -329,58 +362,63 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   load_slice<PAYLOAD, MAXV>(p, t, u0, u1, xv);
   const int my_e = lane < p.k ? my_e_raw : -1;  // lane j: expert of slot j
 
-  // two histograms: all ids, and ids at positions before this token's pairs
-  // (s_a is cleared up to 64 whole chunks, so chunk reads see zeros past E)
+  // Two histograms in one: s_a[e] counts all ids == e in its low 16 bits and
+  // the ids == e at positions before this token's pairs in its high 16 bits
+  // (T*k < 2^16, so sums of these words never carry from the low half into
+  // the high half: a masked sum is a count).  s_a is cleared up to 64 whole
+  // chunks, so chunk reads see zeros past E.
   const int csz = chunk_size(p.E);
-  for (int e = tid; e < kWave * csz; e += kBlock) {
-    s_a[e] = 0;
-    s_b[e] = 0;
-  }
+  for (int e = tid; e < kWave * csz; e += kBlock) s_a[e] = 0;
   // LDS-only barriers from here on: the slice of x loaded above stays in
-  // flight while the histograms are built
+  // flight while the histogram is built
   lds_barrier();
   const int first_pos = t * p.k;
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
     const int q = tid + i * kBlock;
-    if (q < P) {
-      const int e = idv[i];
-      if ((unsigned)e < (unsigned)p.E) {
-        atomicAdd(&s_a[e], 1);
-        if (q < first_pos) atomicAdd(&s_b[e], 1);
-      }
-    }
+    const int e = idv[i];
+    if (q < P && (unsigned)e < (unsigned)p.E) atomicAdd(&s_a[e], q < first_pos ? 0x10001 : 1);
   }
   lds_barrier();
 
-  // Every wave on its own: lane l sums chunk l of csz consecutive experts, a
-  // DPP scan turns the chunk sums into exclusive chunk prefixes, and lane j
-  // reads off, for its slot's expert e:
-  //   A = #valid ids below e, F = #valid ids below the first expert of e's
-  //   rank, B = #ids == e at positions before t*k + j.
+  // Lane j, for its slot's expert e:
+  //   B = #ids == e at positions before t*k + j (histogram of earlier tokens
+  //       plus this token's earlier slots);
+  //   fixed-capacity regions: the row is r*C + #ids in [first, e) + B, where
+  //       first is the first expert of e's rank r -- with L <= kDirectMaxL a
+  //       direct sum over the rank's counts;
+  //   otherwise every wave scans 64 chunk sums of csz experts with DPP and
+  //       reads off A = #valid ids below e (and F = #valid ids below first).
   const bool valid = lane < p.k && (unsigned)my_e < (unsigned)p.E;
   const int e = valid ? my_e : 0;
-  const int first = (e / p.L) * p.L;
-  // all LDS reads of this phase are independent and issued together
-  const int csum = chunk_sum_below(s_a, lane, csz, csz);
-  const int a_part = chunk_sum_below(s_a, e / csz, csz, e % csz);
-  const int f_part = chunk_sum_below(s_a, first / csz, csz, first % csz);
-  const int b_hist = s_b[e];
-  const int cexcl = wave_inclusive_sum_dpp(csum) - csum;
-  const int A = __shfl(cexcl, e / csz, kWave) + a_part;
-  const int F = __shfl(cexcl, first / csz, kWave) + f_part;
+  const int r = rank_of(p, e);
+  const int first = r * p.L;
+  const int b_hist = s_a[e] >> 16;
+  int dup = 0;  // earlier slots of this token with the same expert
+  for (int j2 = 0; j2 < p.k; ++j2) {
+    const int o = __builtin_amdgcn_readlane(my_e, j2);
+    dup += (j2 < lane && o == e) ? 1 : 0;
+  }
   int row = -1;
-  if (valid) {
-    int B = b_hist;
-    for (int j2 = 0; j2 < p.k; ++j2) {
-      const int o = __builtin_amdgcn_readlane(my_e, j2);
-      B += (j2 < lane && o == e) ? 1 : 0;
-    }
-    if (p.C > 0) {
-      const int local = (A - F) + B;
-      if (local < p.C) row = (e / p.L) * p.C + local;
-    } else {
-      row = A + B;
+  if (p.C > 0 && p.L <= kDirectMaxL) {
+    const int local = (rank_prefix(s_a, first, e, p.L) & 0xffff) + b_hist + dup;
+    if (valid && local < p.C) row = r * p.C + local;
+  } else {
+    // all LDS reads of this phase are independent and issued together
+    const int csum = chunk_sum_below(s_a, lane, csz, csz);
+    const int a_part = chunk_sum_below(s_a, e / csz, csz, e % csz);
+    const int f_part = chunk_sum_below(s_a, first / csz, csz, first % csz);
+    const int cexcl = wave_inclusive_sum_dpp(csum) - csum;
+    const int A = (__shfl(cexcl, e / csz, kWave) + a_part) & 0xffff;
+    const int F = (__shfl(cexcl, first / csz, kWave) + f_part) & 0xffff;
+    if (valid) {
+      const int B = b_hist + dup;
+      if (p.C > 0) {
+        const int local = (A - F) + B;
+        if (local < p.C) row = r * p.C + local;
+      } else {
+        row = A + B;
+      }
     }
   }
   row = checked_row(p, row);
@@ -515,6 +553,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams
 }
 
 static_assert(kSmallMaxPairs <= 16 * kBlock, "the fused path loads at most 16 ids per thread");
+static_assert(kSmallMaxPairs < (1 << 16), "packed histogram halves hold counts up to T*k");
 
 template <int PAYLOAD, int MAXV>
 hipError_t launch_paths(const DispatchParams& p, hipStream_t st) {
@@ -581,6 +620,7 @@ hipError_t launch_dispatch(const DispatchParams& in, hipStream_t st) {
   p.col_chunks = (nunits + vpc - 1) / vpc;
   p.nchunks = (int)((P + kChunkPairs - 1) / kChunkPairs);
   p.rows = p.C > 0 ? p.N * p.C : (int)P;
+  p.l_magic = p.L >= 2 ? (uint32_t)(((1ull << 32) + (uint64_t)p.L - 1) / (uint64_t)p.L) : 0u;
   if (P > (size_t)kSmallMaxPairs) {
     char* ws = reinterpret_cast<char*>(p.workspace);
     p.local_rank = reinterpret_cast<int32_t*>(ws);
