@@ -301,6 +301,33 @@ __device__ __forceinline__ int rank_prefix(const int* hist, int first, int e, in
   return s;
 }
 
+// Number of lanes j' < lane (slots of the same token) holding the same
+// non-zero key; key 0 marks an invalid slot.  k <= 8: the slots sit in lanes
+// 0..7 of the first DPP row, so seven row shifts compare every earlier slot
+// (lanes shifted in from outside the row read 0); larger k: a readlane loop.
+__device__ __forceinline__ int earlier_same_slots(int key, int lane, int k) {
+  int n = 0;
+  if (k <= 8) {
+#define MOE_SAME_AT(D)                                                                   \
+  n += (key != 0 && __builtin_amdgcn_update_dpp(0, key, 0x110 + (D), 0xf, 0xf, true) == key) \
+           ? 1 : 0
+    MOE_SAME_AT(1);
+    MOE_SAME_AT(2);
+    MOE_SAME_AT(3);
+    MOE_SAME_AT(4);
+    MOE_SAME_AT(5);
+    MOE_SAME_AT(6);
+    MOE_SAME_AT(7);
+#undef MOE_SAME_AT
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int o = __builtin_amdgcn_readlane(key, j);
+      n += (j < lane && key != 0 && o == key) ? 1 : 0;
+    }
+  }
+  return n;
+}
+
 __device__ __forceinline__ int checked_row(const DispatchParams& p, int row) {
   return (row >= 0 && row < p.rows) ? row : -1;
 }
@@ -379,6 +406,9 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
     const int e = idv[i];
     if (q < P && (unsigned)e < (unsigned)p.E) atomicAdd(&s_a[e], q < first_pos ? 0x10001 : 1);
   }
+  // while the adds land: earlier slots of this token with the same expert
+  const bool valid = lane < p.k && (unsigned)my_e < (unsigned)p.E;
+  const int dup = earlier_same_slots(valid ? my_e + 1 : 0, lane, p.k);
   lds_barrier();
 
   // Lane j, for its slot's expert e:
@@ -389,16 +419,10 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   //       direct sum over the rank's counts;
   //   otherwise every wave scans 64 chunk sums of csz experts with DPP and
   //       reads off A = #valid ids below e (and F = #valid ids below first).
-  const bool valid = lane < p.k && (unsigned)my_e < (unsigned)p.E;
   const int e = valid ? my_e : 0;
   const int r = rank_of(p, e);
   const int first = r * p.L;
   const int b_hist = s_a[e] >> 16;
-  int dup = 0;  // earlier slots of this token with the same expert
-  for (int j2 = 0; j2 < p.k; ++j2) {
-    const int o = __builtin_amdgcn_readlane(my_e, j2);
-    dup += (j2 < lane && o == e) ? 1 : 0;
-  }
   int row = -1;
   if (p.C > 0 && p.L <= kDirectMaxL) {
     const int local = (rank_prefix(s_a, first, e, p.L) & 0xffff) + b_hist + dup;

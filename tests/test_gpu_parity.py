@@ -70,6 +70,15 @@ SWEEP = [
     (1000, 7168, 64, 1, 8, 0, 1, True, None),
     (900, 1024, 32, 8, 4, 0, 1, False, 7),        # fp8, chunked path, duplicates
     (3000, 64, 1024, 8, 32, 0, 0, True, None),     # E at the library maximum
+    # fixed-capacity regions on the one-launch path, with repeated experts in
+    # a token: rows from the in-rank prefix (L <= 32, 16-byte and scalar
+    # reads), from the chunk scan (L > 32), repeats found by row shifts
+    # (k <= 8) and by the readlane loop (k > 8)
+    (256, 512, 32, 8, 4, 2048, 0, False, 5),       # L = 8
+    (120, 256, 96, 8, 4, 960, 0, False, 2),        # L = 24
+    (50, 256, 30, 4, 5, 200, 0, False, None),      # L = 6
+    (100, 512, 64, 12, 8, 800, 1, False, 3),       # k = 12, fp8
+    (64, 256, 256, 8, 2, 512, 0, False, 9),        # L = 128
     (2048, 512, 256, 32, 256, 0, 0, True, None),   # k at the library maximum
 ]
 
