@@ -280,24 +280,29 @@ __device__ __forceinline__ int rank_of(const DispatchParams& p, int e) {
 constexpr int kDirectMaxL = 32;
 
 // Sum of hist[first .. e), first = the rank's first expert, e inside the rank
-// (e < first + L <= first + kDirectMaxL).  With L % 4 == 0 the rank's counts
-// are read as whole 16-byte vectors, all issued before the first is used.
-__device__ __forceinline__ int rank_prefix(const int* hist, int first, int e, int L) {
-  int s = 0;
+// (e < first + L <= first + kDirectMaxL).  With L % 4 == 0 the kDirectMaxL
+// words from first are read as 16-byte vectors, unconditionally and all
+// before the first is used (hist holds kDirectMaxL words of padding past its
+// last expert; words at or past e are masked out).  The arithmetic stays on
+// whole vectors so the reads stay 16-byte LDS reads.
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int rank_prefix(const v4i* hist4, int first, int e, int L) {
   if ((L & 3) == 0) {
-    const int4* h4 = reinterpret_cast<const int4*>(hist + first);
-    int4 q[kDirectMaxL / 4];
+    const v4i* h4 = hist4 + (first >> 2);  // first is a multiple of 4 here
+    v4i q[kDirectMaxL / 4];
 #pragma unroll
-    for (int c = 0; c < kDirectMaxL / 4; ++c) q[c] = 4 * c < L ? h4[c] : make_int4(0, 0, 0, 0);
+    for (int c = 0; c < kDirectMaxL / 4; ++c) q[c] = h4[c];
+    const v4i lanes = {0, 1, 2, 3};
+    const v4i zero = {0, 0, 0, 0};
+    v4i acc = zero;
 #pragma unroll
-    for (int c = 0; c < kDirectMaxL / 4; ++c) {
-      const int x = first + 4 * c;
-      s += (x + 0 < e ? q[c].x : 0) + (x + 1 < e ? q[c].y : 0) + (x + 2 < e ? q[c].z : 0) +
-           (x + 3 < e ? q[c].w : 0);
-    }
-  } else {
-    for (int x = first; x < e; ++x) s += hist[x];
+    for (int c = 0; c < kDirectMaxL / 4; ++c) acc += (lanes + (first + 4 * c) < e) ? q[c] : zero;
+    return acc.x + acc.y + acc.z + acc.w;
   }
+  const int* hist = reinterpret_cast<const int*>(hist4);
+  int s = 0;
+  for (int x = first; x < e; ++x) s += hist[x];
   return s;
 }
 
@@ -308,9 +313,8 @@ __device__ __forceinline__ int rank_prefix(const int* hist, int first, int e, in
 __device__ __forceinline__ int earlier_same_slots(int key, int lane, int k) {
   int n = 0;
   if (k <= 8) {
-#define MOE_SAME_AT(D)                                                                   \
-  n += (key != 0 && __builtin_amdgcn_update_dpp(0, key, 0x110 + (D), 0xf, 0xf, true) == key) \
-           ? 1 : 0
+#define MOE_SAME_AT(D) \
+  n += (int)((key != 0) & (__builtin_amdgcn_update_dpp(0, key, 0x110 + (D), 0xf, 0xf, true) == key))
     MOE_SAME_AT(1);
     MOE_SAME_AT(2);
     MOE_SAME_AT(3);
@@ -341,7 +345,8 @@ __device__ __forceinline__ int checked_row(const DispatchParams& p, int row) {
 // before the histograms, not for the x slice issued after them.
 template <int PAYLOAD, int MAXV, int IPT>
 __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p) {
-  __shared__ __align__(16) int s_a[kMaxExperts];  // histogram (packed pair in the scatter blocks)
+  // histogram (packed pair in the scatter blocks), padded for rank_prefix
+  __shared__ __align__(16) int s_a[kMaxExperts + kDirectMaxL];
   __shared__ int s_b[kMaxExperts + 1];  // block 0: its exclusive scan
   __shared__ int s_wave[kWaves];
   const int P = p.T * p.k;
@@ -422,12 +427,15 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   const int e = valid ? my_e : 0;
   const int r = rank_of(p, e);
   const int first = r * p.L;
-  const int b_hist = s_a[e] >> 16;
   int row = -1;
   if (p.C > 0 && p.L <= kDirectMaxL) {
-    const int local = (rank_prefix(s_a, first, e, p.L) & 0xffff) + b_hist + dup;
+    // the LDS reads of this path are issued together, after the branch
+    const int b_hist = s_a[e] >> 16;
+    const int local =
+        (rank_prefix(reinterpret_cast<const v4i*>(s_a), first, e, p.L) & 0xffff) + b_hist + dup;
     if (valid && local < p.C) row = r * p.C + local;
   } else {
+    const int b_hist = s_a[e] >> 16;
     // all LDS reads of this phase are independent and issued together
     const int csum = chunk_sum_below(s_a, lane, csz, csz);
     const int a_part = chunk_sum_below(s_a, e / csz, csz, e % csz);
