@@ -15,9 +15,10 @@
 //
 // Group-limited routing (same page, MoE Router: plain top-k is the case where
 // the kept groups are all experts): the wave stages its biased logits in LDS,
-// lane g sums the two largest logits of group g, topk_groups arg-max rounds
-// keep the best groups (ties to the lower group id), and the experts of the
-// other groups drop out before the top-k rounds.
+// each group's score is the sum of its two largest logits (64/G lanes per
+// group merging pairs with DPP when G divides 64, else one lane per group),
+// topk_groups arg-max rounds keep the best groups (ties to the lower group
+// id), and the experts of the other groups drop out before the top-k rounds.
 #include "device_common.h"
 #include "launch.h"
 
@@ -95,6 +96,17 @@ __device__ __forceinline__ float slot_sum(float s) {
   return r0 + r1;
 }
 
+// Merge this lane's top two (m1 >= m2) with those of the lane a DPP pattern
+// names: the two largest of the four values, counted with multiplicity.
+template <int CTRL>
+__device__ __forceinline__ void top2_merge(float& m1, float& m2) {
+  const float o1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m1), CTRL, 0xf, 0xf, false));
+  const float o2 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m2), CTRL, 0xf, 0xf, false));
+  const float lo = fminf(m1, o1);
+  m1 = fmaxf(m1, o1);
+  m2 = fmaxf(lo, fmaxf(m2, o2));
+}
+
 // LDS hand-off inside one wavefront (no block barrier: waves exit early).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -140,11 +152,40 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
     for (int i = 0; i < VPL; ++i)
       if (i * kWave + lane < E) sl[i * kWave + lane] = v[i];
     wave_lds_sync();
-    // lane g: group score = sum of the group's two largest biased logits
+    // group score = sum of the group's two largest biased logits
     const int gsz = E / n_groups;
     float gv = -INFINITY;
     int gi = kNone;
-    if (lane < n_groups) {
+    const int lpg = kWave / n_groups;  // lanes per group, when n_groups divides 64
+    if (kWave % n_groups == 0 && lpg <= 16 && gsz % (4 * lpg) == 0 && gsz / lpg <= 16) {
+      // lpg lanes per group: each takes the top two of its gsz/lpg logits
+      // (16-byte LDS reads), then DPP steps inside the group's aligned lanes
+      // merge the pairs; the group's first lane holds the score
+      const int g = lane / lpg, part = lane % lpg, ipl = gsz / lpg;
+      const float4* g4 = reinterpret_cast<const float4*>(sl + g * gsz + part * ipl);
+      float q[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 f = 4 * c < ipl ? g4[c]
+                                     : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        q[4 * c] = f.x;
+        q[4 * c + 1] = f.y;
+        q[4 * c + 2] = f.z;
+        q[4 * c + 3] = f.w;
+      }
+      float m1 = -INFINITY, m2 = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) top2_take(q[c], m1, m2);
+      if (lpg >= 2) top2_merge<0xB1>(m1, m2);   // lane ^ 1
+      if (lpg >= 4) top2_merge<0x4E>(m1, m2);   // lane ^ 2
+      if (lpg >= 8) top2_merge<0x141>(m1, m2);  // mirrored quad
+      if (lpg >= 16) top2_merge<0x140>(m1, m2); // mirrored half-row
+      if (part == 0) {
+        gv = gsz > 1 ? m1 + m2 : m1;
+        gi = g;
+      }
+    } else if (lane < n_groups) {
+      // lane g scans group g
       float m1 = -INFINITY, m2 = -INFINITY;
       if ((gsz & 3) == 0) {
         // 16-byte LDS reads, 4 in flight per round
@@ -181,11 +222,22 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
         gi = kNone;
       }
     }
+    if ((gsz & (gsz - 1)) == 0) {  // power-of-two groups: a shift, not a division
+      const int sh = __ffs(gsz) - 1;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      if (id[i] != kNone && !((kept >> (id[i] / gsz)) & 1ull)) {
-        v[i] = -INFINITY;
-        id[i] = kNone;
+      for (int i = 0; i < VPL; ++i) {
+        if (id[i] != kNone && !((kept >> (id[i] >> sh)) & 1ull)) {
+          v[i] = -INFINITY;
+          id[i] = kNone;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        if (id[i] != kNone && !((kept >> (id[i] / gsz)) & 1ull)) {
+          v[i] = -INFINITY;
+          id[i] = kNone;
+        }
       }
     }
   }

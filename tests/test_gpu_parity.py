@@ -253,6 +253,10 @@ def test_fp8_quantiser_at_extreme_magnitudes(T, k, payload_path):
     (4096, 256, 8, 4, 8, 1.2, False),  # with a popularity bias
     (300, 384, 8, 2, 8, 0.0, True),    # many exact ties
     (64, 64, 64, 5, 4, 0.0, False),    # one expert per group
+    (200, 256, 4, 2, 8, 0.0, True),    # 16 lanes per group, ties
+    (200, 256, 16, 5, 8, 0.0, True),   # 4 lanes per group, ties
+    (100, 256, 32, 6, 8, 0.0, False),  # 2 lanes per group
+    (100, 512, 8, 3, 8, 0.0, False),   # 8 lanes per group, 8 logits per lane
     (50, 256, 1, 1, 8, 0.0, False),    # one group: plain top-k
 ])
 def test_grouped_route(T, E, G, TG, k, zipf, ties):
