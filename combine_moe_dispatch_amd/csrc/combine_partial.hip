@@ -102,7 +102,8 @@ combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ 
                           const int32_t* __restrict__ token_row,
                           const int32_t* __restrict__ ids, const float* __restrict__ w,
                           uint4* __restrict__ partial, int32_t* __restrict__ partial_rank,
-                          int H, int k_rt, int E, int L, int M, int col_chunks) {
+                          int H, int k_rt, int E, int L, uint32_t l_magic, int M,
+                          int col_chunks) {
   constexpr int KV = FP8 ? 2 : 1;
   const int k = K > 0 ? K : k_rt;
   const unsigned b = FP8 ? xcd_local_block(blockIdx.x, gridDim.x) : blockIdx.x;
@@ -126,10 +127,40 @@ combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ 
 #pragma unroll
   for (int g = 0; g < kGroup; ++g) {
     const bool ok = (g < k) & (rj[g] >= 0) & ((unsigned)ej[g] < (unsigned)E);
-    const int rk = max(ej[g], 0) / L;
+    // e / L as a multiply-high by ceil(2^32 / L) (exact: e * L < 2^32)
+    const int rk = L == 1 ? ej[g] : (int)__umulhi((uint32_t)max(ej[g], 0), l_magic);
     rank[g] = ok ? rk : -1;
     rj[g] = g < k ? rj[g] : -1;
     wj[g] = g < k ? wj[g] : 0.0f;
+  }
+  int u[KV];
+#pragma unroll
+  for (int i = 0; i < KV; ++i) u[i] = cc * kBlock * KV + lane + i * kBlock;
+  // no early exit before the gathers: lanes past the row end mask them
+  const bool active = u[0] < nv;
+  // raw loads of every placed slot's vectors, issued before the grouping
+  // arithmetic below so they are in flight meanwhile; each is decoded once,
+  // in its group
+  uint4 yv[kGroup];      // bf16: 8 values
+  uint2 cv[kGroup][KV];  // fp8: 8 codes per vector
+  float sc[kGroup][KV];
+  if constexpr (FP8) {
+    const uint2* y8 = reinterpret_cast<const uint2*>(y);
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+      for (int i = 0; i < KV; ++i) {
+        const bool use = rank[g] >= 0 && u[i] < nv;
+        const size_t r = use ? (size_t)rj[g] : 0;
+        cv[g][i] = use ? load_stream(&y8[r * nv + u[i]]) : make_uint2(0, 0);
+        sc[g][i] = use ? ys[r * nb + u[i] / 16] : 0.0f;  // scales: cached loads
+      }
+  } else {
+    const uint4* y16 = reinterpret_cast<const uint4*>(y);
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g)
+      yv[g] = active && rank[g] >= 0 ? load_stream(&y16[(size_t)rj[g] * nv + u[0]])
+                                    : make_uint4(0, 0, 0, 0);
   }
   // group of slot g = index of its rank among the token's distinct ranks in
   // ascending order; m = number of distinct ranks
@@ -156,33 +187,6 @@ combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ 
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) r = grp[g] == lane ? rank[g] : r;
     partial_rank[(size_t)t * M + lane] = r;
-  }
-  int u[KV];
-#pragma unroll
-  for (int i = 0; i < KV; ++i) u[i] = cc * kBlock * KV + lane + i * kBlock;
-  // no early exit before the gathers: lanes past the row end mask them
-  const bool active = u[0] < nv;
-  // raw loads of every slot's vectors; each is decoded once, in its group
-  uint4 yv[kGroup];      // bf16: 8 values
-  uint2 cv[kGroup][KV];  // fp8: 8 codes per vector
-  float sc[kGroup][KV];
-  if constexpr (FP8) {
-    const uint2* y8 = reinterpret_cast<const uint2*>(y);
-#pragma unroll
-    for (int g = 0; g < kGroup; ++g)
-#pragma unroll
-      for (int i = 0; i < KV; ++i) {
-        const bool use = grp[g] >= 0 && u[i] < nv;
-        const size_t r = use ? (size_t)rj[g] : 0;
-        cv[g][i] = use ? load_stream(&y8[r * nv + u[i]]) : make_uint2(0, 0);
-        sc[g][i] = use ? ys[r * nb + u[i] / 16] : 0.0f;  // scales: cached loads
-      }
-  } else {
-    const uint4* y16 = reinterpret_cast<const uint4*>(y);
-#pragma unroll
-    for (int g = 0; g < kGroup; ++g)
-      yv[g] = active && grp[g] >= 0 ? load_stream(&y16[(size_t)rj[g] * nv + u[0]])
-                                    : make_uint4(0, 0, 0, 0);
   }
   if (!active) return;
   for (int q = 0; q < m; ++q) {
@@ -355,10 +359,11 @@ hipError_t launch_combine_send(const void* y, const float* ys, const int32_t* to
     // 64 vectors of 8 columns per block (bf16), 128 (fp8)
     const int chunks = (H / 8 + kBlock * (payload ? 2 : 1) - 1) / (kBlock * (payload ? 2 : 1));
     const unsigned nblk = (unsigned)T * (unsigned)chunks;
+    const uint32_t l_magic = L >= 2 ? (uint32_t)(((1ull << 32) + L - 1) / L) : 0u;
 #define MOE_SEND_SMALL(FP8, K)                                                              \
   hipLaunchKernelGGL((combine_send_small_kernel<FP8, K>), dim3(nblk), dim3(kBlock), 0, st, y, \
                      ys, token_row, ids, w, reinterpret_cast<uint4*>(partial), partial_rank,  \
-                     H, k, E, L, M, chunks)
+                     H, k, E, L, l_magic, M, chunks)
     if (payload == 0) {
       if (k == kGroup) MOE_SEND_SMALL(false, kGroup); else MOE_SEND_SMALL(false, 0);
     } else {
