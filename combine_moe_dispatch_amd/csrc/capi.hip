@@ -144,6 +144,11 @@ moe_status moe_dispatch_sources(const moe_shape* shape, int32_t num_sources, con
   st = moe_dispatch(&world, x, topk_ids, recv_x, recv_scales, layout, workspace, workspace_bytes,
                     stream);
   if (st != MOE_OK) return st;
+  if (moe::dispatch_bases_per_source(num_sources, shape->num_tokens, shape->top_k))
+    return from_hip(moe::launch_source_from_bases(
+        moe::dispatch_chunk_bases(workspace, world.num_tokens, shape->top_k), num_sources,
+        shape->num_tokens, shape->top_k, shape->num_experts, layout->expert_counts,
+        layout->expert_offsets, source_counts, source_offsets, stream));
   return from_hip(moe::launch_source_metadata(topk_ids, num_sources, shape->num_tokens,
                                               shape->top_k, shape->num_experts,
                                               layout->expert_offsets, source_counts,

@@ -626,6 +626,17 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 }  // namespace
 
+bool dispatch_bases_per_source(int S, int T, int k) {
+  const long P = (long)S * T * k;
+  return S > 1 && P > kSmallMaxPairs && ((long)T * k) % kChunkPairs == 0;
+}
+
+const int32_t* dispatch_chunk_bases(const void* workspace, int total_tokens, int k) {
+  const size_t P = (size_t)total_tokens * (size_t)k;
+  return reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(workspace) +
+                                          align256(4 * P));
+}
+
 size_t dispatch_workspace_bytes(int T, int k, int E) {
   const size_t P = (size_t)T * (size_t)k;
   if (P <= (size_t)kSmallMaxPairs) return 0;

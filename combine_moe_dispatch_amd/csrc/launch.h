@@ -45,6 +45,15 @@ hipError_t launch_route_topk(const float* logits, const float* bias, int T, int 
                              int score, int n_groups, int topk_groups, int32_t* ids, float* w,
                              hipStream_t st);
 
+// Multi-kernel dispatch over S sources of T tokens whose chunks each lie
+// inside one source; its chunk bases then give the per-source metadata.
+bool dispatch_bases_per_source(int S, int T, int k);
+const int32_t* dispatch_chunk_bases(const void* workspace, int total_tokens, int k);
+hipError_t launch_source_from_bases(const int32_t* chunk_base, int S, int T, int k, int E,
+                                    const int32_t* expert_counts, const int32_t* expert_offsets,
+                                    int32_t* source_counts, int32_t* source_offsets,
+                                    hipStream_t st);
+
 hipError_t launch_source_metadata(const int32_t* ids, int S, int T, int k, int E,
                                   const int32_t* expert_offsets, int32_t* source_counts,
                                   int32_t* source_offsets, hipStream_t st);

@@ -9,6 +9,8 @@
 // These kernels add the exchanged part: each source's count vector (written
 // to HBM, the "exchange") and, per expert, the exclusive scan of the counts
 // over sources, i.e. the row where each source's block of that expert begins.
+// When the dispatch took its multi-kernel path with chunks aligned to sources,
+// both come from the chunk bases it already computed, in one launch.
 #include "device_common.h"
 #include "launch.h"
 
@@ -65,7 +67,46 @@ source_offsets_kernel(const int32_t* __restrict__ source_counts,
   }
 }
 
+// When every chunk of the multi-kernel dispatch lies inside one source (T*k a
+// multiple of the chunk size), the chunk bases that dispatch leaves in its
+// workspace already hold, at source s's first chunk, the number of expert e's
+// ids in earlier sources: the per-source offsets and counts are read off them
+// in one pass (one wave per expert, lanes over sources), with no recount.
+__global__ void __launch_bounds__(kBlock)
+source_from_bases_kernel(const int32_t* __restrict__ chunk_base,
+                         const int32_t* __restrict__ expert_counts,
+                         const int32_t* __restrict__ expert_offsets, int S, int E, int cps,
+                         int32_t* __restrict__ source_counts,
+                         int32_t* __restrict__ source_offsets) {
+  const int e = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (e >= E) return;  // whole wave
+  const int lane = lane_id();
+  const int off = expert_offsets[e];
+  const int total = expert_counts[e];
+  for (int s0 = 0; s0 < S; s0 += kWave) {
+    const int s = s0 + lane;
+    const int b = s < S ? chunk_base[(size_t)s * cps * E + e] : 0;
+    const int next = s + 1 < S ? chunk_base[(size_t)(s + 1) * cps * E + e] : total;
+    if (s < S) {
+      source_offsets[(size_t)e * S + s] = off + b;
+      source_counts[(size_t)s * E + e] = next - b;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_source_from_bases(const int32_t* chunk_base, int S, int T, int k, int E,
+                                    const int32_t* expert_counts, const int32_t* expert_offsets,
+                                    int32_t* source_counts, int32_t* source_offsets,
+                                    hipStream_t st) {
+  const int cps = T * k / kChunkPairs;
+  hipLaunchKernelGGL(source_from_bases_kernel,
+                     dim3((E + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, st,
+                     chunk_base, expert_counts, expert_offsets, S, E, cps, source_counts,
+                     source_offsets);
+  return hipGetLastError();
+}
 
 hipError_t launch_source_metadata(const int32_t* ids, int S, int T, int k, int E,
                                   const int32_t* expert_offsets, int32_t* source_counts,

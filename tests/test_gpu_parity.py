@@ -280,6 +280,11 @@ def test_grouped_route(T, E, G, TG, k, zipf, ties):
     (4, 50, 256, 24, 4, 4, 0, 0),
     (3, 100, 256, 16, 4, 4, 160, 1),      # fixed capacity shared by all sources, overflow
     (5, 0, 64, 8, 2, 2, 8, 0),            # no tokens
+    # multi-chunk layouts: capacity overflow with fp8, the one-launch limit,
+    # ids outside [0, E)
+    (6, 256, 512, 64, 8, 8, 1500, 1),
+    (4, 128, 256, 32, 8, 4, 0, 0),
+    (5, 256, 256, 48, 4, 6, 900, 0),
 ])
 def test_dispatch_sources(S, T, H, E, k, N, C, payload):
     """Every source rank dispatching at once: segments in (source, token, slot)
@@ -289,6 +294,9 @@ def test_dispatch_sources(S, T, H, E, k, N, C, payload):
     inp = inputs.generate(S * T, H, E, 77 + S)
     ids = np.stack([inputs.random_ids(T, k, E, 100 + s) for s in range(S)]) if T else \
         np.zeros((S, 0, k), np.int32)
+    if T and C == 900:
+        ids[1, 3, 2] = E + 5  # ids outside [0, E) are skipped and flagged
+        ids[3, 7, 0] = -1
     wts = inputs.random_weights(S * T, k, 5)
     one = api.Shape(T, H, E, k, N, C, payload)
     world = api.world_shape(one, S)
