@@ -61,7 +61,7 @@ __device__ void block_exclusive_scan(const int* cnt, int n, int* excl, int* wave
   const int incl = wave_inclusive_sum(local);
   const int w = threadIdx.x / kWave;
   if (lane_id() == kWave - 1) wave_tot[w] = incl;
-  __syncthreads();
+  lds_barrier();  // LDS only: global stores still in flight are not waited for
   int run = incl - local;
   for (int i = 0; i < w; ++i) run += wave_tot[i];
   for (int i = 0; i < per; ++i)
@@ -74,7 +74,7 @@ __device__ void block_exclusive_scan(const int* cnt, int n, int* excl, int* wave
     for (int i = 0; i < kWaves; ++i) tot += wave_tot[i];
     excl[n] = tot;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Global metadata from the per-expert counts and their exclusive scan.
@@ -481,7 +481,9 @@ __global__ void __launch_bounds__(kBlock) layout_chunk_kernel(DispatchParams p) 
 #pragma unroll
     for (int w2 = 0; w2 < kWaves; ++w2) s_whist[w2][e] = 0;
   }
-  __syncthreads();
+  // LDS-only barriers: they order the histogram exchanges, not the global
+  // stores of the ranks (read by a later kernel)
+  lds_barrier();
 
   const int bits = 32 - __clz(p.E);  // keys 0..E, E marks "no valid id"
   bool bad = false;
@@ -498,18 +500,18 @@ __global__ void __launch_bounds__(kBlock) layout_chunk_kernel(DispatchParams p) 
     const int total = popc64(peers);
     const bool last = before == total - 1;
     if (valid && last) s_whist[w][e] = total;
-    __syncthreads();
+    lds_barrier();
     if (valid) {
       int pre = s_run[e];
       for (int w2 = 0; w2 < w; ++w2) pre += s_whist[w2][e];
       p.local_rank[q] = pre + before;
     }
-    __syncthreads();
+    lds_barrier();
     if (valid && last) {
       atomicAdd(&s_run[e], total);  // sums are order-independent
       s_whist[w][e] = 0;
     }
-    __syncthreads();
+    lds_barrier();
   }
   for (int e = tid; e < p.E; e += kBlock) p.chunk_hist[(size_t)c * p.E + e] = s_run[e];
   bad = __syncthreads_or(bad);
