@@ -81,12 +81,6 @@ __device__ __forceinline__ void store_stream(uint2* p, uint2 v) {
   const u32x2 t = {v.x, v.y};
   __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
 }
-__device__ __forceinline__ float load_stream(const float* p) {
-  return __builtin_nontemporal_load(p);
-}
-__device__ __forceinline__ void store_stream(float* p, float v) {
-  __builtin_nontemporal_store(v, p);
-}
 
 // Workgroups are handed to the 8 XCDs of the chip in turn (workgroup b runs
 // on XCD b % 8), and each XCD has its own L2.  This renumbers the n
@@ -107,17 +101,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Inclusive/exclusive sums over a wave64 with shuffles.
-__device__ __forceinline__ int wave_inclusive_sum(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  return v;
 }
 
 // Inclusive prefix sum over a wave64 with DPP: Hillis-Steele shifts inside

@@ -58,7 +58,7 @@ __device__ void block_exclusive_scan(const int* cnt, int n, int* excl, int* wave
   int local = 0;
   for (int i = 0; i < per; ++i)
     if (start + i < n) local += cnt[start + i];
-  const int incl = wave_inclusive_sum(local);
+  const int incl = wave_inclusive_sum_dpp(local);
   const int w = threadIdx.x / kWave;
   if (lane_id() == kWave - 1) wave_tot[w] = incl;
   lds_barrier();  // LDS only: global stores still in flight are not waited for
