@@ -19,3 +19,10 @@ def pytest_configure(config):
     if not os.path.exists(os.path.join(ROOT, "oracle", "libmoe_oracle.so")):
         import oracle
         oracle.build()
+    if not os.path.exists(os.path.join(ROOT, "tests", "c_abi", "c_abi_smoke")):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "c_abi_build", os.path.join(ROOT, "tests", "c_abi", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
