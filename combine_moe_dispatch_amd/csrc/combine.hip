@@ -42,14 +42,15 @@ __device__ __forceinline__ void fold_rows(float (&acc)[8], const uint4 (&yv)[N],
   }
 }
 
-// K > 0: top-k fixed at compile time, so the token's rows and weights are
-// read first, as wide uniform loads, before anything else waits; K == 0: k
-// at run time.  Rows are gathered kGroup at a time.  Grid: x = column chunk,
-// y = token.
+// K > 0 (at most kGroup): top-k fixed at compile time, so the token's rows
+// and weights are read first, as straight-line uniform loads, before anything
+// else waits; K == 0: k at run time.  Rows are gathered kGroup at a time.
+// Grid: x = column chunk, y = token.
 template <int K>
 __global__ void __launch_bounds__(kBlock)
 combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ token_row,
                     const float* __restrict__ w, uint4* __restrict__ out, int H, int k_rt) {
+  static_assert(K <= kGroup, "compile-time top-k is gathered in one group");
   const int k = K > 0 ? K : k_rt;
   const int t = blockIdx.y;
   const int nvec = H / 8;
@@ -98,6 +99,7 @@ __global__ void __launch_bounds__(kBlock)
 combine_fp8_kernel(const uint2* __restrict__ y, const float* __restrict__ ys,
                    const int32_t* __restrict__ token_row, const float* __restrict__ w,
                    uint4* __restrict__ out, int H, int k_rt, int col_chunks) {
+  static_assert(K <= kGroup, "compile-time top-k is gathered in one group");
   const int k = K > 0 ? K : k_rt;
   const unsigned b = xcd_local_block(blockIdx.x, gridDim.x);
   const int t = b / col_chunks;
@@ -165,27 +167,28 @@ hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_r
   const int per_block = payload == 0 ? kBlock : 2 * kBlock;  // vectors of 8 columns
   const int col_chunks = (H / 8 + per_block - 1) / per_block;
   const unsigned blocks = (unsigned)T * (unsigned)col_chunks;
-  if (payload == 0) {
-    const dim3 grid((unsigned)col_chunks, (unsigned)T);
-    if (k == 8)
-      hipLaunchKernelGGL(combine_bf16_kernel<8>, grid, dim3(kBlock), 0, st,
-                         reinterpret_cast<const uint4*>(y), token_row, w,
-                         reinterpret_cast<uint4*>(out), H, k);
-    else
-      hipLaunchKernelGGL(combine_bf16_kernel<0>, grid, dim3(kBlock), 0, st,
-                         reinterpret_cast<const uint4*>(y), token_row, w,
-                         reinterpret_cast<uint4*>(out), H, k);
-  } else
-  {
-    if (k == 8)
-      hipLaunchKernelGGL(combine_fp8_kernel<8>, dim3(blocks), dim3(kBlock), 0, st,
-                         reinterpret_cast<const uint2*>(y), ys, token_row, w,
-                         reinterpret_cast<uint4*>(out), H, k, col_chunks);
-    else
-      hipLaunchKernelGGL(combine_fp8_kernel<0>, dim3(blocks), dim3(kBlock), 0, st,
-                         reinterpret_cast<const uint2*>(y), ys, token_row, w,
-                         reinterpret_cast<uint4*>(out), H, k, col_chunks);
+  // compile-time top-k for the common values (the token's rows are then one
+  // straight-line uniform load), run-time k otherwise
+#define MOE_COMBINE(KK)                                                                   \
+  do {                                                                                    \
+    if (payload == 0)                                                                     \
+      hipLaunchKernelGGL(combine_bf16_kernel<KK>, dim3((unsigned)col_chunks, (unsigned)T), \
+                         dim3(kBlock), 0, st, reinterpret_cast<const uint4*>(y), token_row, \
+                         w, reinterpret_cast<uint4*>(out), H, k);                          \
+    else                                                                                  \
+      hipLaunchKernelGGL(combine_fp8_kernel<KK>, dim3(blocks), dim3(kBlock), 0, st,       \
+                         reinterpret_cast<const uint2*>(y), ys, token_row, w,             \
+                         reinterpret_cast<uint4*>(out), H, k, col_chunks);                \
+  } while (0)
+  switch (k) {
+    case 1: MOE_COMBINE(1); break;
+    case 2: MOE_COMBINE(2); break;
+    case 4: MOE_COMBINE(4); break;
+    case 6: MOE_COMBINE(6); break;
+    case 8: MOE_COMBINE(8); break;
+    default: MOE_COMBINE(0); break;
   }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

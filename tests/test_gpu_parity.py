@@ -78,6 +78,8 @@ SWEEP = [
     (120, 256, 96, 8, 4, 960, 0, False, 2),        # L = 24
     (50, 256, 30, 4, 5, 200, 0, False, None),      # L = 6
     (100, 512, 64, 12, 8, 800, 1, False, 3),       # k = 12, fp8
+    (100, 512, 64, 6, 8, 600, 0, True, None),      # k = 6 (compile-time combine)
+    (100, 512, 64, 6, 8, 600, 1, False, 2),        # k = 6, fp8, repeats
     (64, 256, 256, 8, 2, 512, 0, False, 9),        # L = 128
     (2048, 512, 256, 32, 256, 0, 0, True, None),   # k at the library maximum
 ]
