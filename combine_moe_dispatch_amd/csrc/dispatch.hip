@@ -49,6 +49,7 @@ constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / kWave;
 constexpr int kDevCapacity = 1;
 constexpr int kDevBadId = 2;
+constexpr int kComputeUnits = 256;  // MI355X
 
 // Exclusive scan of n <= kMaxExperts LDS counts into excl[0..n] (excl[n] is
 // the total).  All threads of the block must call it.
@@ -652,13 +653,19 @@ hipError_t launch_dispatch(const DispatchParams& in, hipStream_t st) {
   const size_t P = (size_t)p.T * p.k;
   // Column chunks of whole units (8 columns bf16, 16 fp8), balanced; a
   // multiple of 128 columns, so an fp8 scale block never straddles two
-  // blocks.  One unit per thread, except where the fused path's per-block
-  // recount of all T*k ids is heavy (T*k > 2048): there two units per thread
-  // halve the number of recounting blocks.
-  const bool wide = P > 2048 && P <= (size_t)kSmallMaxPairs;
-  const int budget = wide ? 2 * kBlock : kBlock;
+  // blocks.  fp8 units (each quantised on its own) and the chunked path: at
+  // most one unit per thread.  bf16 on the fused path, where every block
+  // recounts all T*k ids: up to two units per thread, so fewer blocks
+  // recount, but no fewer chunks than it takes to give each of the 256
+  // compute units a block.
   const int align = kFp8Block / (p.payload ? 16 : 8);
-  p.col_chunks = (nunits + budget - 1) / budget;
+  if (p.payload == 0 && P <= (size_t)kSmallMaxPairs) {
+    const int fewest = (nunits + 2 * kBlock - 1) / (2 * kBlock);
+    const int most = (nunits + kBlock - 1) / kBlock;
+    p.col_chunks = max(fewest, min((kComputeUnits + p.T - 1) / max(p.T, 1), most));
+  } else {
+    p.col_chunks = (nunits + kBlock - 1) / kBlock;
+  }
   int vpc = (nunits + p.col_chunks - 1) / p.col_chunks;
   vpc = (vpc + align - 1) / align * align;
   p.vec_per_chunk = vpc;
