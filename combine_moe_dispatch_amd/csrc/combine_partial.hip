@@ -113,8 +113,9 @@ combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ 
   const int nb = H / kFp8Block;
   const int lane = threadIdx.x;
   // slot g: row, rank (-1 if skipped), weight -- uniform values
-  // (straight-line: every load is unconditional, slot indices clamped, so
-  // all of them are issued before the first wait)
+  // (straight-line: every load is unconditional, slot indices clamped, and
+  // nothing below branches on a loaded value, so all of them are issued
+  // before the first wait)
   int rj[kGroup], ej[kGroup], rank[kGroup];
   float wj[kGroup];
 #pragma unroll
@@ -124,11 +125,14 @@ combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ 
     ej[g] = ids[q];
     wj[g] = w[q];
   }
+  // e / L as a multiply-high by ceil(2^32 / L) (exact: e * L < 2^32); with
+  // L == 1 the magic is 0 and the rank is e itself
+  const uint32_t l_one = L == 1 ? 0xffffffffu : 0u;
 #pragma unroll
   for (int g = 0; g < kGroup; ++g) {
-    const bool ok = (g < k) & (rj[g] >= 0) & ((unsigned)ej[g] < (unsigned)E);
-    // e / L as a multiply-high by ceil(2^32 / L) (exact: e * L < 2^32)
-    const int rk = L == 1 ? ej[g] : (int)__umulhi((uint32_t)max(ej[g], 0), l_magic);
+    const uint32_t eu = (uint32_t)ej[g];
+    const bool ok = (g < k) & (rj[g] >= 0) & (eu < (uint32_t)E);
+    const int rk = (int)(__umulhi(eu, l_magic) | (eu & l_one));
     rank[g] = ok ? rk : -1;
     rj[g] = g < k ? rj[g] : -1;
     wj[g] = g < k ? wj[g] : 0.0f;
