@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--topk-groups", type=int, default=1, help="groups kept per token")
     ap.add_argument("--combine", choices=("single", "two-stage"), default="single",
                     help="receiver-only combine, or sender-side partial reduction + receive")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the timings of the adjacent paths (partial-reduction combine, "
+                         "receive-side shuffle, group-limited router) in the default run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (PMC scale factor)")
     return ap.parse_args()
@@ -152,7 +155,8 @@ def copy_calibration():
 
 
 class BufferSet:
-    def __init__(self, api, w, shape, inp, torch, np, two_stage=False, split=False):
+    def __init__(self, api, w, shape, inp, torch, np, two_stage=False, split=False,
+                 grouped=False):
         dev = "cuda"
         self.logits = torch.from_numpy(inp.logits).to(dev)
         self.bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
@@ -170,6 +174,9 @@ class BufferSet:
         M = api.partial_slots(shape) if two_stage else 0
         self.partial = torch.empty(w.tokens, M, w.H, dtype=torch.int16, device=dev)
         self.prank = torch.empty(w.tokens, M, dtype=torch.int32, device=dev)
+        if grouped:  # the group-limited router's own outputs
+            self.gids = torch.empty(w.tokens, w.k, dtype=torch.int32, device=dev)
+            self.gw = torch.empty(w.tokens, w.k, dtype=torch.float32, device=dev)
         if split:  # dense grouped-GEMM rows, and regions the send half writes back into
             dense = api.Shape(shape.num_tokens, shape.hidden, shape.num_experts, shape.top_k,
                               shape.num_ranks, 0, shape.payload)
@@ -192,7 +199,12 @@ def run_gpu(args, w, inp):
     nbytes = algorithmic_bytes(w)
     per_step = nbytes["dispatch"] + nbytes["combine"] + nbytes["route"]
     S = args.sets or min(64, max(2, math.ceil(2 * MALL_BYTES / per_step)))
-    sets = [BufferSet(api, w, shape, inp, torch, np, args.combine == "two-stage", args.split)
+    # adjacent paths timed beside the main one (cold only), on the same sets
+    nxt = not args.no_next
+    grouping = next_grouping(w) if nxt and args.groups <= 1 else None
+    two_stage_t = args.combine == "two-stage" or nxt
+    split_t = args.split or nxt
+    sets = [BufferSet(api, w, shape, inp, torch, np, two_stage_t, split_t, grouping is not None)
             for _ in range(S)]
     stream = torch.cuda.Stream()
 
@@ -231,6 +243,10 @@ def run_gpu(args, w, inp):
         dispatch(s)
         combine(s)
 
+    def route_grouped(s):
+        api.moe_route_topk_grouped(s.logits, s.bias, w.k, w.score, grouping[0], grouping[1],
+                                   s.gids, s.gw, stream=stream)
+
     def dispatch_recv(s):  # receive regions -> dense grouped-GEMM input
         api.moe_dispatch_recv(shape, s.recv, s.rs, s.lay, s.gx, s.gs, s.goff, stream=stream)
 
@@ -243,9 +259,11 @@ def run_gpu(args, w, inp):
             dispatch(s)
             api.moe_expert_scale(shape, s.recv, s.rs, s.lay, s.alpha, s.y, s.ys, stream=stream)
             combine(s)
+            if two_stage_t and not two_stage:
+                combine_send(s)
     stream.synchronize()
     status = int(sets[0].lay.status.item())
-    partial_rows = int((sets[0].prank >= 0).sum().item()) if two_stage else 0
+    partial_rows = int((sets[0].prank >= 0).sum().item()) if two_stage_t else 0
     placed_rows = int((sets[0].lay.token_row >= 0).sum().item())
 
     def capture(fn_list, n, rotate):
@@ -299,7 +317,7 @@ def run_gpu(args, w, inp):
             "dispatch_us": time_graph(g_disp, K, reps=3),
             "combine_us": time_graph(g_comb, K, reps=3),
         }
-        if two_stage:
+        if two_stage or (two_stage_t and mode == "cold"):
             g_send = capture([combine_send], K, rotate)
             g_recv = capture([combine_recv], K, rotate)
             with torch.cuda.stream(stream):
@@ -308,7 +326,7 @@ def run_gpu(args, w, inp):
             r["combine_send_us"] = time_graph(g_send, K, reps=3)
             r["combine_recv_us"] = time_graph(g_recv, K, reps=3)
             del g_send, g_recv
-        if args.split:
+        if args.split or (split_t and mode == "cold"):
             g_dr = capture([dispatch_recv], K, rotate)
             g_cs = capture([combine_send_back], K, rotate)
             with torch.cuda.stream(stream):
@@ -317,11 +335,37 @@ def run_gpu(args, w, inp):
             r["dispatch_recv_us"] = time_graph(g_dr, K, reps=3)
             r["combine_send_back_us"] = time_graph(g_cs, K, reps=3)
             del g_dr, g_cs
+        if grouping is not None and mode == "cold":
+            g_rg = capture([route_grouped], K, rotate)
+            with torch.cuda.stream(stream):
+                g_rg.replay()
+            r["route_grouped_us"] = time_graph(g_rg, K, reps=3)
+            del g_rg
         res[mode] = r
         del g_step, g_route, g_disp, g_comb
     if not args.no_floor:
         res["floor"] = stream_floor(torch, stream, time_graph, payload_bytes(w), min(K, 100))
     return res
+
+
+def two_stage_bytes(w, partial_rows):
+    """Algorithmic bytes of the partial-reduction combine.  Send: the k rows
+    and (row, id, weight) per pair in, one bf16 row per used (token, rank) slot
+    and the slot ranks out; recv: those rows and ranks in, the token out."""
+    M = min(w.k, w.N)
+    send = w.tokens * (nbytes_row(w) * w.k + 12 * w.k + 4 * M) + partial_rows * 2 * w.H
+    recv = partial_rows * 2 * w.H + w.tokens * (4 * M + 2 * w.H)
+    return send, recv
+
+
+def next_grouping(w):
+    """(groups, groups kept) for the group-limited router timing: DeepSeek-V3's
+    8 groups with 4 kept where the experts divide into 8 groups that hold k;
+    None where they do not."""
+    G, kept = 8, 4
+    if w.E % G or kept * (w.E // G) < w.k:
+        return None
+    return G, kept
 
 
 def payload_bytes(w):
@@ -456,12 +500,7 @@ def main():
     print(f"[bench] gpu timing done: {json.dumps(g)}", file=sys.stderr, flush=True)
     nbytes = algorithmic_bytes(w)
     if args.combine == "two-stage":
-        # send: the k rows and (row, id, weight) per pair in, one bf16 row per
-        # used (token, rank) slot and the slot ranks out; recv: those back in,
-        # the token out
-        M = min(w.k, w.N)
-        send = w.tokens * (nbytes_row(w) * w.k + 12 * w.k + 4 * M) + g["partial_rows"] * 2 * w.H
-        recv = g["partial_rows"] * 2 * w.H + w.tokens * (4 * M + 2 * w.H)
+        send, recv = two_stage_bytes(w, g["partial_rows"])
         nbytes["combine"] = send + recv
         nbytes["combine_send"], nbytes["combine_recv"] = send, recv
     cold = g["cold"]
@@ -506,20 +545,35 @@ def main():
                      "traffic": read_traffic(profile_tag(args), dom)},
         "device_status": g["status"],
     }
+    send_b, recv_b = two_stage_bytes(w, g["partial_rows"])
+    # receive-side shuffle: each placed row read once and written once, plus
+    # (counts, offsets) per expert read and the dense offsets written
+    moved = 2 * g["placed_rows"] * nbytes_row(w) + 8 * w.E + 4 * (w.E + 1)
+    extra = {}
     if "combine_send_us" in cold:
-        line["two_stage_combine"] = {
+        extra["combine_partial"] = {
             "send_us": round(cold["combine_send_us"], 3), "recv_us": round(cold["combine_recv_us"], 3),
-            "partial_rows": g["partial_rows"], "rows_per_token": round(g["partial_rows"] / w.tokens, 3)}
+            "partial_rows": g["partial_rows"], "rows_per_token": round(g["partial_rows"] / w.tokens, 3),
+            "send_GBps": round(send_b / (cold["combine_send_us"] * 1e-6) / 1e9, 1),
+            "recv_GBps": round(recv_b / (cold["combine_recv_us"] * 1e-6) / 1e9, 1)}
     if "dispatch_recv_us" in cold:
-        # each placed row is read once and written once, plus (counts, offsets) per expert
-        # read and the dense offsets written
-        moved = 2 * g["placed_rows"] * nbytes_row(w) + 8 * w.E + 4 * (w.E + 1)
-        line["split"] = {
+        extra["split"] = {
             "dispatch_recv_us": round(cold["dispatch_recv_us"], 3),
             "combine_send_us": round(cold["combine_send_back_us"], 3),
             "bytes_each": moved,
             "dispatch_recv_GBps": round(moved / (cold["dispatch_recv_us"] * 1e-6) / 1e9, 1),
             "combine_send_GBps": round(moved / (cold["combine_send_back_us"] * 1e-6) / 1e9, 1)}
+    if "route_grouped_us" in cold:
+        G, kept = next_grouping(w)
+        extra["route_grouped"] = {"groups": G, "groups_kept": kept,
+                                  "route_us": round(cold["route_grouped_us"], 3)}
+    if args.combine == "two-stage":
+        line["two_stage_combine"] = extra.pop("combine_partial")
+    if args.split:
+        line["split"] = extra.pop("split")
+    if extra:
+        # adjacent paths on the same inputs, cold, one graph of K launches each
+        line["next"] = extra
     if "warm" in g:
         wm = g["warm"]
         wus = wm["dispatch_us"] + wm["combine_us"]

@@ -69,3 +69,9 @@ def test_bench_prints_one_contract_line():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
     assert d["device_status"] == 0
+    # the adjacent paths timed in the default run
+    nx = d["next"]
+    assert set(nx) == {"combine_partial", "split", "route_grouped"}
+    assert nx["combine_partial"]["send_us"] > 0 and nx["combine_partial"]["recv_us"] > 0
+    assert nx["split"]["dispatch_recv_us"] > 0 and nx["split"]["combine_send_us"] > 0
+    assert nx["route_grouped"]["route_us"] > 0
