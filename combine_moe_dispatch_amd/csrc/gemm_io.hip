@@ -12,11 +12,13 @@
 // Higher Throughput with Multi-Node DeepSeek Deployment", Quantization), so
 // the calls need no host round trip and can be captured in a graph.
 //
-// Each block rebuilds dense[] in LDS (placed count per expert, then a scan),
-// block 0 publishes it, and the block moves kRows dense rows: a binary search
-// in LDS finds a row's expert, and the rows move as 16-byte streaming
-// accesses, every load of a pass issued before its stores (fp8 rows carry
-// their H/128 scales along).
+// One wave per block, no LDS and no barrier: every wave loads all experts'
+// counts and segment offsets (PER consecutive experts per lane), forms the
+// dense offsets with a DPP scan, and finds the expert of each of its dense
+// rows by a compare in every lane and a ballot.  Wave 0 publishes the dense
+// offsets.  A row then moves as 16-byte streaming accesses, all loads of a
+// pass (KV vectors per lane, indices clamped so none is conditional) issued
+// before its stores; fp8 rows carry their H/128 scales along.
 #include "device_common.h"
 #include "launch.h"
 
@@ -24,134 +26,120 @@ namespace moe {
 
 namespace {
 
-constexpr int kBlock = 256;
-constexpr int kRows = 4;  // dense rows per block
-
-// dense[0..E]: exclusive scan of the placed rows per expert (a segment may be
-// cut short by its rank's capacity).
-// Also copies the segment offsets into off[0..E).
-__device__ void dense_offsets(const int32_t* counts, const int32_t* offsets, int E, int L, int C,
-                              int* dense, int* off, int* wave_tot) {
-  const int per = (E + kBlock - 1) / kBlock;  // <= 4
-  const int start = threadIdx.x * per;
-  int cnt[4], o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {  // all loads first (clamped), one round trip
-    const int e = min(start + i, E - 1);
-    cnt[i] = counts[e];
-    o[i] = offsets[e];
-  }
-  int placed[4];
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = start + i;
-    int p = 0;
-    if (i < per && e < E) {
-      p = cnt[i];
-      if (C > 0) p = max(0, min(p, (e / L) * C + C - o[i]));
-      off[e] = o[i];
-    }
-    placed[i] = p;
-    local += p;
-  }
-  const int incl = wave_inclusive_sum_dpp(local);
-  const int w = threadIdx.x / kWave;
-  if (lane_id() == kWave - 1) wave_tot[w] = incl;
-  __syncthreads();
-  int run = incl - local;
-  for (int i = 0; i < w; ++i) run += wave_tot[i];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (i < per && start + i < E) {
-      dense[start + i] = run;
-      run += placed[i];
-    }
-  }
-  if (threadIdx.x == kBlock - 1) {
-    int tot = 0;
-    for (int i = 0; i < kBlock / kWave; ++i) tot += wave_tot[i];
-    dense[E] = tot;
-  }
-  __syncthreads();
-}
-
-// Largest e with dense[e] <= i (dense is non-decreasing, dense[0] = 0).
-__device__ __forceinline__ int find_expert(const int* dense, int E, int i) {
-  int lo = 0, hi = E;  // answer in [lo, hi)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (dense[mid] <= i)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  return lo;
-}
-
-constexpr int kVecsPerThread = 4;  // 16-byte vectors of one row per thread and pass
-
-// PACK: receive regions -> dense rows; otherwise dense rows -> regions.  The
-// block's kRows rows are located first (binary search in LDS), then each pass
-// issues every load of those rows before the first store.
-template <bool PACK>
-__global__ void __launch_bounds__(kBlock)
+// PACK: receive regions -> dense rows; otherwise dense rows -> regions.
+// Block b moves dense rows [b*R, b*R + R).
+template <bool PACK, int PER, int KV>
+__global__ void __launch_bounds__(kWave)
 gemm_io_kernel(const uint8_t* __restrict__ src, const float* __restrict__ src_scales,
                uint8_t* __restrict__ dst, float* __restrict__ dst_scales,
                const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-               int32_t* __restrict__ dense_out, int E, int L, int C, int row_bytes, int nb) {
-  __shared__ int s_dense[kMaxExperts + 1];
-  __shared__ int s_off[kMaxExperts];
-  __shared__ int s_wave[kBlock / kWave];
-  dense_offsets(counts, offsets, E, L, C, s_dense, s_off, s_wave);
-  if (PACK && blockIdx.x == 0)
-    for (int e = threadIdx.x; e <= E; e += kBlock) dense_out[e] = s_dense[e];
-  const int total = s_dense[E];
+               int32_t* __restrict__ dense_out, int E, int C, uint32_t l_magic, int row_bytes,
+               int nb, int R) {
+  const int lane = threadIdx.x;
+  const int e0 = lane * PER;
+  int cnt[PER], off[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {  // every load first (clamped): one round trip
+    const int e = min(e0 + i, E - 1);
+    cnt[i] = counts[e];
+    off[i] = offsets[e];
+  }
+  // placed rows per expert: the count, cut at the end of the expert's rank
+  // region for fixed capacity (rank = e / L by a multiply-high with
+  // ceil(2^32 / L), exact for e * L < 2^32; l_magic = 0 means L = 1)
+  int placed[PER];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t e = (uint32_t)(e0 + i);
+    int pl = max(cnt[i], 0);
+    if (C > 0) {
+      const int r = (int)(l_magic ? __umulhi(e, l_magic) : e);
+      pl = max(0, min(pl, (r + 1) * C - off[i]));
+    }
+    placed[i] = (int)e < E ? pl : 0;
+    local += placed[i];
+  }
+  const int incl = wave_inclusive_sum_dpp(local);
+  const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+  int dense[PER];
+  {
+    int run = incl - local;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      dense[i] = run;
+      run += placed[i];
+    }
+  }
+  if (PACK && blockIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (e0 + i < E) dense_out[e0 + i] = dense[i];
+    if (lane == 0) dense_out[E] = total;
+  }
   const int nvec = row_bytes / 16;
-  bool ok[kRows];
-  size_t from[kRows], to[kRows];
+  const int i_end = min(total, (int)(blockIdx.x + 1) * R);
+  for (int i = blockIdx.x * R; i < i_end; ++i) {
+    // the one expert segment holding dense row i
+    int hit = -1;
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    const int i = blockIdx.x * kRows + r;
-    ok[r] = i < total;  // uniform
-    const int e = ok[r] ? find_expert(s_dense, E, i) : 0;
-    const size_t region_row = (size_t)(s_off[e] + (i - s_dense[e]));
-    from[r] = PACK ? region_row : (size_t)i;
-    to[r] = PACK ? (size_t)i : region_row;
-  }
-  for (int v0 = 0; v0 < nvec; v0 += kVecsPerThread * kBlock) {
-    uint4 buf[kRows][kVecsPerThread];
+    for (int q = 0; q < PER; ++q)
+      if (dense[q] <= i && i < dense[q] + placed[q]) hit = off[q] + (i - dense[q]);
+    const uint64_t m = __ballot(hit >= 0);
+    if (m == 0) continue;  // not reached: i < total lies in some segment
+    const int region_row = __builtin_amdgcn_readlane(hit, (int)__builtin_ctzll(m));
+    const size_t from = PACK ? (size_t)region_row : (size_t)i;
+    const size_t to = PACK ? (size_t)i : (size_t)region_row;
+    const uint4* s4 = reinterpret_cast<const uint4*>(src + from * row_bytes);
+    uint4* d4 = reinterpret_cast<uint4*>(dst + to * row_bytes);
+    for (int v0 = 0; v0 < nvec; v0 += KV * kWave) {
+      uint4 buf[KV];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const uint4* s4 = reinterpret_cast<const uint4*>(src + from[r] * row_bytes);
+      for (int j = 0; j < KV; ++j) buf[j] = load_stream(&s4[min(v0 + j * kWave + lane, nvec - 1)]);
 #pragma unroll
-      for (int j = 0; j < kVecsPerThread; ++j) {
-        const int v = v0 + j * kBlock + threadIdx.x;
-        buf[r][j] = ok[r] && v < nvec ? load_stream(&s4[v]) : make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < KV; ++j) {
+        const int v = v0 + j * kWave + lane;
+        if (v < nvec) store_stream(&d4[v], buf[j]);
       }
     }
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      uint4* d4 = reinterpret_cast<uint4*>(dst + to[r] * row_bytes);
-#pragma unroll
-      for (int j = 0; j < kVecsPerThread; ++j) {
-        const int v = v0 + j * kBlock + threadIdx.x;
-        if (ok[r] && v < nvec) store_stream(&d4[v], buf[r][j]);
-      }
-    }
-  }
-  if (src_scales) {
-    for (int b0 = 0; b0 < nb; b0 += kBlock) {
-      float sc[kRows];
-      const int b = b0 + threadIdx.x;
-#pragma unroll
-      for (int r = 0; r < kRows; ++r) sc[r] = ok[r] && b < nb ? src_scales[from[r] * nb + b] : 0.0f;
-#pragma unroll
-      for (int r = 0; r < kRows; ++r)
-        if (ok[r] && b < nb) dst_scales[to[r] * nb + b] = sc[r];
-    }
+    if (src_scales)
+      for (int b = lane; b < nb; b += kWave) dst_scales[to * nb + b] = src_scales[from * nb + b];
   }
 }
+
+template <bool PACK, int PER>
+void launch_kv(int nvec, dim3 grid, hipStream_t st, const uint8_t* s, const float* ss,
+               uint8_t* d, float* ds, const int32_t* counts, const int32_t* offsets,
+               int32_t* dense_out, int E, int C, uint32_t l_magic, int row_bytes, int nb, int R) {
+  // vectors per lane and pass: enough for a whole row where it fits in 16
+  if (nvec <= 4 * kWave)
+    hipLaunchKernelGGL((gemm_io_kernel<PACK, PER, 4>), grid, dim3(kWave), 0, st, s, ss, d, ds,
+                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb, R);
+  else if (nvec <= 8 * kWave)
+    hipLaunchKernelGGL((gemm_io_kernel<PACK, PER, 8>), grid, dim3(kWave), 0, st, s, ss, d, ds,
+                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb, R);
+  else
+    hipLaunchKernelGGL((gemm_io_kernel<PACK, PER, 16>), grid, dim3(kWave), 0, st, s, ss, d, ds,
+                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb, R);
+}
+
+template <bool PACK>
+void launch_per(int nvec, dim3 grid, hipStream_t st, const uint8_t* s, const float* ss,
+                uint8_t* d, float* ds, const int32_t* counts, const int32_t* offsets,
+                int32_t* dense_out, int E, int C, uint32_t l_magic, int row_bytes, int nb, int R) {
+  // experts per lane: E <= 64 * PER
+  if (E <= 4 * kWave)
+    launch_kv<PACK, 4>(nvec, grid, st, s, ss, d, ds, counts, offsets, dense_out, E, C, l_magic,
+                       row_bytes, nb, R);
+  else if (E <= 8 * kWave)
+    launch_kv<PACK, 8>(nvec, grid, st, s, ss, d, ds, counts, offsets, dense_out, E, C, l_magic,
+                       row_bytes, nb, R);
+  else
+    launch_kv<PACK, 16>(nvec, grid, st, s, ss, d, ds, counts, offsets, dense_out, E, C, l_magic,
+                        row_bytes, nb, R);
+}
+
+static_assert(kMaxExperts <= 16 * kWave, "the widest kernel holds 16 experts per lane");
 
 }  // namespace
 
@@ -161,17 +149,21 @@ hipError_t launch_gemm_io(bool pack, const void* src, const float* src_scales, v
                           int payload, hipStream_t st) {
   const int row_bytes = payload == 0 ? 2 * H : H;
   const int nb = payload == 0 ? 0 : H / kFp8Block;
-  const unsigned blocks = (unsigned)max(1, (max_rows + kRows - 1) / kRows);
+  // one dense row per wave up to 8192 rows, then 4 (every wave loads all E
+  // counts and offsets: a few KB from L2)
+  const int R = max_rows <= 8192 ? 1 : 4;
+  const dim3 grid((unsigned)max(1, (max_rows + R - 1) / R));
+  const uint32_t l_magic = L >= 2 ? (uint32_t)(((1ull << 32) + L - 1) / L) : 0u;
   const uint8_t* s = reinterpret_cast<const uint8_t*>(src);
   uint8_t* d = reinterpret_cast<uint8_t*>(dst);
+  const float* ss = payload ? src_scales : nullptr;
+  const int nvec = row_bytes / 16;
   if (pack)
-    hipLaunchKernelGGL((gemm_io_kernel<true>), dim3(blocks), dim3(kBlock), 0, st, s,
-                       payload ? src_scales : nullptr, d, dst_scales, counts, offsets, dense_out,
-                       E, L, C, row_bytes, nb);
+    launch_per<true>(nvec, grid, st, s, ss, d, dst_scales, counts, offsets, dense_out, E, C,
+                     l_magic, row_bytes, nb, R);
   else
-    hipLaunchKernelGGL((gemm_io_kernel<false>), dim3(blocks), dim3(kBlock), 0, st, s,
-                       payload ? src_scales : nullptr, d, dst_scales, counts, offsets, dense_out,
-                       E, L, C, row_bytes, nb);
+    launch_per<false>(nvec, grid, st, s, ss, d, dst_scales, counts, offsets, dense_out, E, C,
+                      l_magic, row_bytes, nb, R);
   return hipGetLastError();
 }
 
