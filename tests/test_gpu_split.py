@@ -39,6 +39,10 @@ def _host(t, fp8):
     (200, 512, 64, 4, 8, 0, 0, None),         # packed regions
     (96, 1024, 32, 8, 4, 240, 1, 1),          # fp8 with overflow
     (0, 256, 8, 2, 2, 16, 0, None),           # no tokens
+    (64, 512, 384, 8, 16, 192, 0, None),      # 384 experts: 8 per lane
+    (32, 256, 1024, 8, 16, 0, 1, None),       # 1024 experts: 16 per lane, fp8
+    (24, 8704, 64, 4, 4, 0, 0, None),         # rows of more than 1024 vectors: two passes
+    (1040, 256, 64, 8, 8, 1000, 1, 2),        # > 8192 rows: 4 rows per wave, fp8, overflow
 ])
 def test_split_chain(T, H, E, k, N, C, payload, hot):
     print(f"[case] split T={T} H={H} E={E} k={k} N={N} C={C} p={payload}", flush=True)
