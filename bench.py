@@ -375,14 +375,16 @@ def payload_bytes(w):
 
 def stream_floor(torch, stream, time_graph, nbytes, n):
     """What the memory system sustains at this size: plain streaming read and
-    write of `nbytes` with the same 16-byte non-temporal accesses, and an
-    empty launch, timed like the kernels (graphs of n launches over rotating
-    buffers, cold); the best of three grid sizes."""
+    write of `nbytes` with 16-byte accesses, and an empty launch, timed like
+    the kernels (graphs of n launches over rotating buffers, cold).  Read: a
+    non-temporal grid-stride loop, the best of three grid sizes.  Write: the
+    best of that loop and of 64 KB blocks stored with each cache policy."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "combine_moe_dispatch_amd", "libmoe_ceiling.so"))
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     lib.moe_ceiling_read.argtypes = [vp, sz, vp, i32, vp]
     lib.moe_ceiling_write.argtypes = [vp, sz, i32, vp]
+    lib.moe_ceiling_write_blocked.argtypes = [vp, sz, i32, vp]
     lib.moe_ceiling_empty.argtypes = [vp]
     nbytes = (nbytes + 15) // 16 * 16
     S = min(64, max(2, math.ceil(2 * MALL_BYTES / nbytes)))
@@ -410,6 +412,10 @@ def stream_floor(torch, stream, time_graph, nbytes, n):
                                                        sink.data_ptr(), b, st)) for b in grids)
     wr = min(timed(lambda i, b=b: lib.moe_ceiling_write(bufs[i % S].data_ptr(), nvec, b, st))
              for b in grids)
+    # 64 KB per block with each cache policy (at some sizes faster than the loop)
+    wr = min([wr] + [timed(lambda i, c=c: lib.moe_ceiling_write_blocked(bufs[i % S].data_ptr(),
+                                                                       nvec, c, st))
+                     for c in (0, 1, 2)])
     em = timed(lambda i: lib.moe_ceiling_empty(st))
     del bufs
     torch.cuda.empty_cache()

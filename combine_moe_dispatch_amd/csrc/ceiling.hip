@@ -31,6 +31,26 @@ stream_write_kernel(u32x4* __restrict__ p, size_t n, unsigned v) {
     __builtin_nontemporal_store(val, &p[i]);
 }
 
+// Block b writes vectors [b*4096, b*4096 + 4096): 16 per thread, each
+// instruction of the block covering 4 KB, through a buffer descriptor for the
+// block's range with the given cache policy (2 = non-temporal, 0 = default,
+// 16 = system-coherent write-through).  At some sizes this pattern and policy
+// beat the grid-stride loop, so the floor takes the best of both.
+template <int POLICY>
+__global__ void __launch_bounds__(256)
+blocked_write_kernel(u32x4* __restrict__ p, size_t n, unsigned v) {
+  const u32x4 val = {v, v, v, v};
+  const size_t base = (size_t)blockIdx.x * 4096;
+  const int count = (int)min((size_t)4096, n - base);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(p + base, (short)0, count * 16, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int i = j * 256 + (int)threadIdx.x;
+    if (i < count) __builtin_amdgcn_raw_buffer_store_b128(val, rs, i * 16, 0, POLICY);
+  }
+}
+
 __global__ void __launch_bounds__(256)
 stream_copy_kernel(const u32x4* __restrict__ s, u32x4* __restrict__ d, size_t n) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -60,6 +80,22 @@ extern "C" int moe_ceiling_write(void* p, size_t nvec, int blocks, hipStream_t s
   if (!p || !aligned16(p) || blocks < 1 || blocks > 65535) return 1;
   hipLaunchKernelGGL(stream_write_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<u32x4*>(p), nvec, 7u);
+  return (int)hipGetLastError();
+}
+
+// policy: 0 = non-temporal, 1 = default, 2 = system-coherent write-through.
+extern "C" int moe_ceiling_write_blocked(void* p, size_t nvec, int policy, hipStream_t stream) {
+  if (!p || !aligned16(p) || nvec == 0 || policy < 0 || policy > 2) return 1;
+  const size_t blocks = (nvec + 4095) / 4096;
+  if (blocks > 0x7fffffff) return 1;
+  u32x4* q = static_cast<u32x4*>(p);
+  const dim3 grid((unsigned)blocks);
+  if (policy == 0)
+    hipLaunchKernelGGL(blocked_write_kernel<2>, grid, dim3(256), 0, stream, q, nvec, 7u);
+  else if (policy == 1)
+    hipLaunchKernelGGL(blocked_write_kernel<0>, grid, dim3(256), 0, stream, q, nvec, 7u);
+  else
+    hipLaunchKernelGGL(blocked_write_kernel<16>, grid, dim3(256), 0, stream, q, nvec, 7u);
   return (int)hipGetLastError();
 }
 

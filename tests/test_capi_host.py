@@ -169,6 +169,7 @@ def test_stream_floor_library_loads_and_rejects_bad_arguments():
     lib.moe_ceiling_read.argtypes = [vp, sz, vp, i32, vp]
     lib.moe_ceiling_write.argtypes = [vp, sz, i32, vp]
     lib.moe_ceiling_copy.argtypes = [vp, vp, sz, i32, vp]
+    lib.moe_ceiling_write_blocked.argtypes = [vp, sz, i32, vp]
     lib.moe_ceiling_empty.argtypes = [vp]
     assert lib.moe_ceiling_read(None, 16, 256, 64, None) == 1
     assert lib.moe_ceiling_read(4096, 16, None, 64, None) == 1
@@ -176,3 +177,7 @@ def test_stream_floor_library_loads_and_rejects_bad_arguments():
     assert lib.moe_ceiling_write(4096, 16, 0, None) == 1
     assert lib.moe_ceiling_write(4096, 16, 70000, None) == 1
     assert lib.moe_ceiling_copy(4096, 4104, 16, 64, None) == 1
+    assert lib.moe_ceiling_write_blocked(None, 16, 0, None) == 1
+    assert lib.moe_ceiling_write_blocked(4104, 16, 0, None) == 1
+    assert lib.moe_ceiling_write_blocked(4096, 0, 0, None) == 1
+    assert lib.moe_ceiling_write_blocked(4096, 16, 3, None) == 1
