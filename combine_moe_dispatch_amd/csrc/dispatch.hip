@@ -281,24 +281,28 @@ __device__ __forceinline__ int rank_of(const DispatchParams& p, int e) {
 constexpr int kDirectMaxL = 32;
 
 // Sum of hist[first .. e), first = the rank's first expert, e inside the rank
-// (e < first + L <= first + kDirectMaxL).  With L % 4 == 0 the kDirectMaxL
-// words from first are read as 16-byte vectors, unconditionally and all
-// before the first is used (hist holds kDirectMaxL words of padding past its
-// last expert; words at or past e are masked out).  The arithmetic stays on
-// whole vectors so the reads stay 16-byte LDS reads.
+// (e < first + L <= first + 4 * NV, NV <= kDirectMaxL / 4).  With L % 4 == 0
+// the 4 * NV words from first are read as 16-byte vectors, unconditionally and
+// all before the first is used (hist holds kDirectMaxL words of padding past
+// its last expert; words at or past e are masked out).  The arithmetic stays
+// on whole vectors so the reads stay 16-byte LDS reads.  NV is fixed at
+// compile time from L (2 for L <= 8, 4 for L <= 16, else 8), so a rank of
+// few experts reads and sums only its own words.
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+template <int NV>
 __device__ __forceinline__ int rank_prefix(const v4i* hist4, int first, int e, int L) {
+  static_assert(NV <= kDirectMaxL / 4, "reads stay inside the padding");
   if ((L & 3) == 0) {
     const v4i* h4 = hist4 + (first >> 2);  // first is a multiple of 4 here
-    v4i q[kDirectMaxL / 4];
+    v4i q[NV];
 #pragma unroll
-    for (int c = 0; c < kDirectMaxL / 4; ++c) q[c] = h4[c];
+    for (int c = 0; c < NV; ++c) q[c] = h4[c];
     const v4i lanes = {0, 1, 2, 3};
     const v4i zero = {0, 0, 0, 0};
     v4i acc = zero;
 #pragma unroll
-    for (int c = 0; c < kDirectMaxL / 4; ++c) acc += (lanes + (first + 4 * c) < e) ? q[c] : zero;
+    for (int c = 0; c < NV; ++c) acc += (lanes + (first + 4 * c) < e) ? q[c] : zero;
     return acc.x + acc.y + acc.z + acc.w;
   }
   const int* hist = reinterpret_cast<const int*>(hist4);
@@ -343,8 +347,9 @@ __device__ __forceinline__ int checked_row(const DispatchParams& p, int row) {
 // IPT = ids per thread (T*k <= IPT * kBlock).  Every global load below is
 // unconditional (indices clamped into range, values masked afterwards), so
 // the compiler can count loads in flight exactly and wait only for the ids
-// before the histograms, not for the x slice issued after them.
-template <int PAYLOAD, int MAXV, int IPT>
+// before the histograms, not for the x slice issued after them.  NVR: the
+// 16-byte vectors rank_prefix reads (at least L / 4 on its direct path).
+template <int PAYLOAD, int MAXV, int IPT, int NVR>
 __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p) {
   // histogram (packed pair in the scatter blocks), padded for rank_prefix
   __shared__ __align__(16) int s_a[kMaxExperts + kDirectMaxL];
@@ -433,7 +438,8 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
     // the LDS reads of this path are issued together, after the branch
     const int b_hist = s_a[e] >> 16;
     const int local =
-        (rank_prefix(reinterpret_cast<const v4i*>(s_a), first, e, p.L) & 0xffff) + b_hist + dup;
+        (rank_prefix<NVR>(reinterpret_cast<const v4i*>(s_a), first, e, p.L) & 0xffff) + b_hist +
+        dup;
     if (valid && local < p.C) row = r * p.C + local;
   } else {
     const int b_hist = s_a[e] >> 16;
@@ -590,20 +596,31 @@ __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams
 static_assert(kSmallMaxPairs <= 16 * kBlock, "the fused path loads at most 16 ids per thread");
 static_assert(kSmallMaxPairs < (1 << 16), "packed histogram halves hold counts up to T*k");
 
+template <int PAYLOAD, int MAXV, int NVR>
+void launch_fused(const DispatchParams& p, hipStream_t st) {
+  const long P = (long)p.T * p.k;
+  const unsigned blocks = 1u + (unsigned)p.T * (unsigned)p.col_chunks;
+  if (P <= kBlock * 4)
+    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 4, NVR>), dim3(blocks), dim3(kBlock),
+                       0, st, p);
+  else if (P <= kBlock * 8)
+    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 8, NVR>), dim3(blocks), dim3(kBlock),
+                       0, st, p);
+  else
+    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 16, NVR>), dim3(blocks),
+                       dim3(kBlock), 0, st, p);
+}
+
 template <int PAYLOAD, int MAXV>
 hipError_t launch_paths(const DispatchParams& p, hipStream_t st) {
   const long P = (long)p.T * p.k;
   if (P <= kSmallMaxPairs) {
-    const unsigned blocks = 1u + (unsigned)p.T * (unsigned)p.col_chunks;
-    if (P <= kBlock * 4)
-      hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 4>), dim3(blocks), dim3(kBlock), 0,
-                         st, p);
-    else if (P <= kBlock * 8)
-      hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 8>), dim3(blocks), dim3(kBlock), 0,
-                         st, p);
+    if (p.L <= 8)
+      launch_fused<PAYLOAD, MAXV, 2>(p, st);
+    else if (p.L <= 16)
+      launch_fused<PAYLOAD, MAXV, 4>(p, st);
     else
-      hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 16>), dim3(blocks), dim3(kBlock),
-                         0, st, p);
+      launch_fused<PAYLOAD, MAXV, kDirectMaxL / 4>(p, st);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunks), dim3(kBlock), 0, st, p);
@@ -620,9 +637,10 @@ hipError_t launch_paths(const DispatchParams& p, hipStream_t st) {
 template <int PAYLOAD>
 hipError_t launch_payload(const DispatchParams& p, hipStream_t st) {
   const int maxv = (p.vec_per_chunk + kBlock - 1) / kBlock;
+  // column chunks hold at most two units per thread (launch_dispatch)
   if (maxv <= 1) return launch_paths<PAYLOAD, 1>(p, st);
   if (maxv <= 2) return launch_paths<PAYLOAD, 2>(p, st);
-  return launch_paths<PAYLOAD, 4>(p, st);
+  return hipErrorInvalidValue;
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
