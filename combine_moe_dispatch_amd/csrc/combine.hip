@@ -98,11 +98,12 @@ template <int K>
 __global__ void __launch_bounds__(kBlock)
 combine_fp8_kernel(const uint2* __restrict__ y, const float* __restrict__ ys,
                    const int32_t* __restrict__ token_row, const float* __restrict__ w,
-                   uint4* __restrict__ out, int H, int k_rt, int col_chunks) {
+                   uint4* __restrict__ out, int H, int k_rt, int col_chunks,
+                   uint32_t cc_magic) {
   static_assert(K <= kGroup, "compile-time top-k is gathered in one group");
   const int k = K > 0 ? K : k_rt;
   const unsigned b = xcd_local_block(blockIdx.x, gridDim.x);
-  const int t = b / col_chunks;
+  const int t = (int)udiv_magic(b, (uint32_t)col_chunks, cc_magic);
   const int cc = b - t * col_chunks;
   const int nv = H / 8;
   const int nb = H / kFp8Block;
@@ -167,6 +168,7 @@ hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_r
   const int per_block = payload == 0 ? kBlock : 2 * kBlock;  // vectors of 8 columns
   const int col_chunks = (H / 8 + per_block - 1) / per_block;
   const unsigned blocks = (unsigned)T * (unsigned)col_chunks;
+  const uint32_t cc_magic = udiv_magic_of((uint32_t)col_chunks);
   // compile-time top-k for the common values (the token's rows are then one
   // straight-line uniform load), run-time k otherwise
 #define MOE_COMBINE(KK)                                                                   \
@@ -178,7 +180,7 @@ hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_r
     else                                                                                  \
       hipLaunchKernelGGL(combine_fp8_kernel<KK>, dim3(blocks), dim3(kBlock), 0, st,       \
                          reinterpret_cast<const uint2*>(y), ys, token_row, w,             \
-                         reinterpret_cast<uint4*>(out), H, k, col_chunks);                \
+                         reinterpret_cast<uint4*>(out), H, k, col_chunks, cc_magic);      \
   } while (0)
   switch (k) {
     case 1: MOE_COMBINE(1); break;

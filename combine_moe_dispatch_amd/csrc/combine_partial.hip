@@ -103,11 +103,11 @@ combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ 
                           const int32_t* __restrict__ ids, const float* __restrict__ w,
                           uint4* __restrict__ partial, int32_t* __restrict__ partial_rank,
                           int H, int k_rt, int E, int L, uint32_t l_magic, int M,
-                          int col_chunks) {
+                          int col_chunks, uint32_t cc_magic) {
   constexpr int KV = FP8 ? 2 : 1;
   const int k = K > 0 ? K : k_rt;
   const unsigned b = FP8 ? xcd_local_block(blockIdx.x, gridDim.x) : blockIdx.x;
-  const int t = b / col_chunks;
+  const int t = (int)udiv_magic(b, (uint32_t)col_chunks, cc_magic);
   const int cc = b - t * col_chunks;
   const int nv = H / 8;  // 8-column vectors per row
   const int nb = H / kFp8Block;
@@ -233,9 +233,9 @@ combine_send_kernel(const uint4* __restrict__ y, const float* __restrict__ ys,
                     const int32_t* __restrict__ token_row, const int32_t* __restrict__ ids,
                     const float* __restrict__ w, uint4* __restrict__ partial,
                     int32_t* __restrict__ partial_rank, int H, int k, int E, int L, int M,
-                    int col_chunks) {
+                    int col_chunks, uint32_t cc_magic) {
   constexpr int kCols = FP8 ? 16 : 8;  // columns per thread
-  const int t = blockIdx.x / col_chunks;
+  const int t = (int)udiv_magic(blockIdx.x, (uint32_t)col_chunks, cc_magic);
   const int cc = blockIdx.x - t * col_chunks;
   const int nvec = H / kCols;
   const int lane = threadIdx.x;
@@ -310,9 +310,10 @@ combine_send_kernel(const uint4* __restrict__ y, const float* __restrict__ ys,
 template <int MM>
 __global__ void __launch_bounds__(kBlock)
 combine_recv_kernel(const uint4* __restrict__ partial, const int32_t* __restrict__ partial_rank,
-                    uint4* __restrict__ out, int H, int M_rt, int col_chunks) {
+                    uint4* __restrict__ out, int H, int M_rt, int col_chunks,
+                    uint32_t cc_magic) {
   const int M = MM > 0 ? MM : M_rt;
-  const int t = blockIdx.x / col_chunks;
+  const int t = (int)udiv_magic(blockIdx.x, (uint32_t)col_chunks, cc_magic);
   const int cc = blockIdx.x - t * col_chunks;
   const int nvec = H / 8;
   const int v = cc * kBlock + threadIdx.x;
@@ -367,7 +368,7 @@ hipError_t launch_combine_send(const void* y, const float* ys, const int32_t* to
 #define MOE_SEND_SMALL(FP8, K)                                                              \
   hipLaunchKernelGGL((combine_send_small_kernel<FP8, K>), dim3(nblk), dim3(kBlock), 0, st, y, \
                      ys, token_row, ids, w, reinterpret_cast<uint4*>(partial), partial_rank,  \
-                     H, k, E, L, l_magic, M, chunks)
+                     H, k, E, L, l_magic, M, chunks, udiv_magic_of((uint32_t)chunks))
     if (payload == 0) {
       if (k == kGroup) MOE_SEND_SMALL(false, kGroup); else MOE_SEND_SMALL(false, 0);
     } else {
@@ -380,12 +381,12 @@ hipError_t launch_combine_send(const void* y, const float* ys, const int32_t* to
     hipLaunchKernelGGL((combine_send_kernel<false, 8>), dim3(blocks), dim3(kBlock), 0, st,
                        reinterpret_cast<const uint4*>(y), ys, token_row, ids, w,
                        reinterpret_cast<uint4*>(partial), partial_rank, H, k, E, E / N, M,
-                       col_chunks);
+                       col_chunks, udiv_magic_of((uint32_t)col_chunks));
   else
     hipLaunchKernelGGL((combine_send_kernel<true, 4>), dim3(blocks), dim3(kBlock), 0, st,
                        reinterpret_cast<const uint4*>(y), ys, token_row, ids, w,
                        reinterpret_cast<uint4*>(partial), partial_rank, H, k, E, E / N, M,
-                       col_chunks);
+                       col_chunks, udiv_magic_of((uint32_t)col_chunks));
   return hipGetLastError();
 }
 
@@ -398,11 +399,13 @@ hipError_t launch_combine_recv(const void* partial, const int32_t* partial_rank,
   if (M == kGroup)
     hipLaunchKernelGGL(combine_recv_kernel<kGroup>, grid, dim3(kBlock), 0, st,
                        reinterpret_cast<const uint4*>(partial), partial_rank,
-                       reinterpret_cast<uint4*>(out), H, M, col_chunks);
+                       reinterpret_cast<uint4*>(out), H, M, col_chunks,
+                       udiv_magic_of((uint32_t)col_chunks));
   else
     hipLaunchKernelGGL(combine_recv_kernel<0>, grid, dim3(kBlock), 0, st,
                        reinterpret_cast<const uint4*>(partial), partial_rank,
-                       reinterpret_cast<uint4*>(out), H, M, col_chunks);
+                       reinterpret_cast<uint4*>(out), H, M, col_chunks,
+                       udiv_magic_of((uint32_t)col_chunks));
   return hipGetLastError();
 }
 

@@ -132,6 +132,18 @@ __device__ __forceinline__ uint64_t wave_match(uint32_t key, int bits) {
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
+// n / d without a division, for any n < 2^32 and d >= 1: with
+// m = floor((2^32 - 1) / d), umulhi(n, m) is floor(n / d) or one less (the
+// product undershoots n / d by less than n / 2^32 < 1), and one remainder
+// check corrects it.  Uniform operands keep it to a few scalar instructions.
+__host__ __device__ __forceinline__ uint32_t udiv_magic_of(uint32_t d) {
+  return 0xffffffffu / d;
+}
+__device__ __forceinline__ uint32_t udiv_magic(uint32_t n, uint32_t d, uint32_t m) {
+  const uint32_t q = __umulhi(n, m);
+  return q + (n - q * d >= d ? 1u : 0u);
+}
+
 __device__ __forceinline__ uint64_t lanes_below() {
   const int lane = lane_id();
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));

@@ -384,18 +384,18 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
     return;
   }
 
-  const int b = blockIdx.x - 1;
-  const int t = b / p.col_chunks;
-  const int cc = b - t * p.col_chunks;
-  const int u0 = cc * p.vec_per_chunk;
-  const int u1 = min(u0 + p.vec_per_chunk, units_per_row(p));
-
-  // issue every load first: this token's k ids, the whole id list (a few
-  // per thread) and this block's slice of the token row
-  const int my_e_raw = p.ids[t * p.k + min(lane, p.k - 1)];
+  // issue every load first: the whole id list (a few per thread; these do
+  // not depend on the block's token), this token's k ids and this block's
+  // slice of the token row
   int idv[IPT];
 #pragma unroll
   for (int i = 0; i < IPT; ++i) idv[i] = p.ids[min(tid + i * kBlock, P - 1)];
+  const int b = blockIdx.x - 1;
+  const int t = (int)udiv_magic((uint32_t)b, (uint32_t)p.col_chunks, p.cc_magic);
+  const int cc = b - t * p.col_chunks;
+  const int u0 = cc * p.vec_per_chunk;
+  const int u1 = min(u0 + p.vec_per_chunk, p.H >> (PAYLOAD ? 4 : 3));
+  const int my_e_raw = p.ids[t * p.k + min(lane, p.k - 1)];
   uint4 xv[MAXV][Unit<PAYLOAD>::kXV];
   load_slice<PAYLOAD, MAXV>(p, t, u0, u1, xv);
   const int my_e = lane < p.k ? my_e_raw : -1;  // lane j: expert of slot j
@@ -559,10 +559,10 @@ __global__ void __launch_bounds__(kBlock) layout_scan_kernel(DispatchParams p) {
 // Chunked path, kernel 3: rows from the chunk bases, then the scatter.
 template <int PAYLOAD, int MAXV>
 __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams p) {
-  const int t = blockIdx.x / p.col_chunks;
+  const int t = (int)udiv_magic(blockIdx.x, (uint32_t)p.col_chunks, p.cc_magic);
   const int cc = blockIdx.x - t * p.col_chunks;
   const int u0 = cc * p.vec_per_chunk;
-  const int u1 = min(u0 + p.vec_per_chunk, units_per_row(p));
+  const int u1 = min(u0 + p.vec_per_chunk, p.H >> (PAYLOAD ? 4 : 3));
   const int lane = lane_id();
   // Loads in dependency order, all unconditional (indices clamped, values
   // masked), so each wait covers only what it needs: the slot's id and
@@ -688,6 +688,7 @@ hipError_t launch_dispatch(const DispatchParams& in, hipStream_t st) {
   vpc = (vpc + align - 1) / align * align;
   p.vec_per_chunk = vpc;
   p.col_chunks = (nunits + vpc - 1) / vpc;
+  p.cc_magic = udiv_magic_of((uint32_t)p.col_chunks);
   p.nchunks = (int)((P + kChunkPairs - 1) / kChunkPairs);
   p.rows = p.C > 0 ? p.N * p.C : (int)P;
   p.l_magic = p.L >= 2 ? (uint32_t)(((1ull << 32) + (uint64_t)p.L - 1) / (uint64_t)p.L) : 0u;

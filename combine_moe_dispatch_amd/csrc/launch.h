@@ -36,6 +36,7 @@ struct DispatchParams {
   int col_chunks;     // blocks per token in the scatter
   int vec_per_chunk;  // row units per block (8 columns bf16, 16 columns fp8)
   uint32_t l_magic;   // ceil(2^32 / L) for L >= 2: e / L == umulhi(e, l_magic) for e < 2^16
+  uint32_t cc_magic;  // udiv_magic_of(col_chunks)
 };
 
 size_t dispatch_workspace_bytes(int T, int k, int E);
