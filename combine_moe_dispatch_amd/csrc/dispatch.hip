@@ -82,7 +82,7 @@ __device__ void block_exclusive_scan(const int* cnt, int n, int* excl, int* wave
 __device__ void write_metadata(const DispatchParams& p, const int* cnt, const int* excl,
                                bool bad) {
   for (int e = threadIdx.x; e < p.E; e += kBlock) {
-    const int r = e / p.L;
+    const int r = p.L == 1 ? e : (int)__umulhi((uint32_t)e, p.l_magic);
     const int first = excl[r * p.L];
     const int base = p.C > 0 ? r * p.C : first;
     p.expert_counts[e] = cnt[e];
@@ -468,70 +468,85 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
 // ---------------------------------------------------------------------------
 // Chunked path, kernel 1: ranks inside a chunk and the chunk's histogram.
 // ---------------------------------------------------------------------------
+// The chunk's 1024 pairs form 16 groups of 64 (one wave's pairs per pass), in
+// pair order.  Each wave ranks its pairs among equal experts in its group by
+// ballot matching and the group's last equal pair records the group count;
+// one pass over the groups per expert turns the counts into exclusive
+// prefixes (and the chunk total), so a pair's rank in the chunk is its
+// group's prefix plus its rank in the group.  Three barriers in all.
+static_assert(kChunkPairs < (1 << 16), "in-chunk prefixes are held in 16 bits");
+
 __global__ void __launch_bounds__(kBlock) layout_chunk_kernel(DispatchParams p) {
-  __shared__ int s_run[kMaxExperts];
-  __shared__ int s_whist[kWaves][kMaxExperts];
   constexpr int kSubs = kChunkPairs / kBlock;
+  constexpr int kGroups = kSubs * kWaves;
+  // [group][expert]: counts <= 64, then prefixes <= kChunkPairs: 16 bits
+  __shared__ __align__(16) uint16_t s_grp[kGroups * kMaxExperts];
   const int c = blockIdx.x;
   const int P = p.T * p.k;
+  const int E = p.E;
   const int tid = threadIdx.x;
   const int w = tid / kWave;
 
   int idv[kSubs];
 #pragma unroll
-  for (int s = 0; s < kSubs; ++s) {
-    const int q = c * kChunkPairs + s * kBlock + tid;
-    idv[s] = q < P ? p.ids[q] : p.E;
-  }
-  for (int e = tid; e < p.E; e += kBlock) {
-    s_run[e] = 0;
-#pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) s_whist[w2][e] = 0;
+  for (int s = 0; s < kSubs; ++s) idv[s] = p.ids[min(c * kChunkPairs + s * kBlock + tid, P - 1)];
+  {
+    int4* g4 = reinterpret_cast<int4*>(s_grp);
+    for (int i = tid; i < kGroups * E / 8; i += kBlock) g4[i] = make_int4(0, 0, 0, 0);
   }
   // LDS-only barriers: they order the histogram exchanges, not the global
   // stores of the ranks (read by a later kernel)
   lds_barrier();
 
-  const int bits = 32 - __clz(p.E);  // keys 0..E, E marks "no valid id"
+  const int bits = 32 - __clz(E);  // keys 0..E, E marks "no valid id"
   bool bad = false;
+  int before[kSubs];
 #pragma unroll
   for (int s = 0; s < kSubs; ++s) {
     const int q = c * kChunkPairs + s * kBlock + tid;
     const bool has = q < P;
     const int e = idv[s];
-    const bool valid = has && (unsigned)e < (unsigned)p.E;
+    const bool valid = has && (unsigned)e < (unsigned)E;
     bad |= has && !valid;
-    const uint32_t key = valid ? (uint32_t)e : (uint32_t)p.E;
+    const uint32_t key = valid ? (uint32_t)e : (uint32_t)E;
     const uint64_t peers = wave_match(key, bits);
-    const int before = popc64(peers & lanes_below());
+    before[s] = popc64(peers & lanes_below());
     const int total = popc64(peers);
-    const bool last = before == total - 1;
-    if (valid && last) s_whist[w][e] = total;
-    lds_barrier();
-    if (valid) {
-      int pre = s_run[e];
-      for (int w2 = 0; w2 < w; ++w2) pre += s_whist[w2][e];
-      p.local_rank[q] = pre + before;
-    }
-    lds_barrier();
-    if (valid && last) {
-      atomicAdd(&s_run[e], total);  // sums are order-independent
-      s_whist[w][e] = 0;
-    }
-    lds_barrier();
+    if (valid && before[s] == total - 1) s_grp[(s * kWaves + w) * E + e] = (uint16_t)total;
   }
-  for (int e = tid; e < p.E; e += kBlock) p.chunk_hist[(size_t)c * p.E + e] = s_run[e];
+  lds_barrier();
+  for (int e = tid; e < E; e += kBlock) {
+    int n[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) n[g] = s_grp[g * E + e];
+    int run = 0;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      s_grp[g * E + e] = (uint16_t)run;
+      run += n[g];
+    }
+    p.chunk_hist[(size_t)c * E + e] = run;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int s = 0; s < kSubs; ++s) {
+    const int q = c * kChunkPairs + s * kBlock + tid;
+    const int e = idv[s];
+    if (q < P && (unsigned)e < (unsigned)E)
+      p.local_rank[q] = s_grp[(s * kWaves + w) * E + e] + before[s];
+  }
   bad = __syncthreads_or(bad);
   if (tid == 0) p.chunk_bad[c] = bad ? 1 : 0;
 }
 
 // Chunked path, kernel 2: per-chunk bases (exclusive over chunks, in place),
-// global counts, scan and metadata.  One block.
+// global counts, scan and metadata.  One block; a thread per expert issues
+// the loads of 32 chunks at once.
 __global__ void __launch_bounds__(kBlock) layout_scan_kernel(DispatchParams p) {
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_excl[kMaxExperts + 1];
   __shared__ int s_wave[kWaves];
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 32;
   const int tid = threadIdx.x;
   for (int e = tid; e < p.E; e += kBlock) {
     int run = 0;
@@ -539,7 +554,7 @@ __global__ void __launch_bounds__(kBlock) layout_scan_kernel(DispatchParams p) {
       int h[kBatch];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i)
-        h[i] = c0 + i < p.nchunks ? p.chunk_hist[(size_t)(c0 + i) * p.E + e] : 0;
+        h[i] = p.chunk_hist[(size_t)min(c0 + i, p.nchunks - 1) * p.E + e];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i)
         if (c0 + i < p.nchunks) {
