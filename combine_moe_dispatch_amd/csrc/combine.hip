@@ -45,8 +45,9 @@ __device__ __forceinline__ void fold_rows(float (&acc)[8], const uint4 (&yv)[N],
 // K > 0 (at most kGroup): top-k fixed at compile time, so the token's rows
 // and weights are read first, as straight-line uniform loads, before anything
 // else waits; K == 0: k at run time.  Rows are gathered kGroup at a time.
-// Grid: x = column chunk, y = token.
-template <int K>
+// DS: the output row is stored with device scope instead of non-temporally
+// (chosen for large outputs).  Grid: x = column chunk, y = token.
+template <int K, bool DS>
 __global__ void __launch_bounds__(kBlock)
 combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ token_row,
                     const float* __restrict__ w, uint4* __restrict__ out, int H, int k_rt) {
@@ -84,7 +85,10 @@ combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ tok
   o.y = pack_bf16x2(acc[2], acc[3]);
   o.z = pack_bf16x2(acc[4], acc[5]);
   o.w = pack_bf16x2(acc[6], acc[7]);
-  store_stream(&out[(size_t)t * nvec + v], o);
+  if constexpr (DS)
+    store_device_scope(out + (size_t)t * nvec, nvec * 16, v * 16, o);
+  else
+    store_stream(&out[(size_t)t * nvec + v], o);
 }
 
 // fp8: a lane owns two 8-code vectors, u and u + 64 of its block's 128, so
@@ -169,14 +173,23 @@ hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_r
   const int col_chunks = (H / 8 + per_block - 1) / per_block;
   const unsigned blocks = (unsigned)T * (unsigned)col_chunks;
   const uint32_t cc_magic = udiv_magic_of((uint32_t)col_chunks);
+  // bf16 output of 32 MB or more: device-scope stores (measured 3 % faster on
+  // the 4096-token skewed prefill, slower at decode sizes)
+  const bool ds = (size_t)T * (size_t)H * 2 >= ((size_t)32 << 20);
   // compile-time top-k for the common values (the token's rows are then one
   // straight-line uniform load), run-time k otherwise
 #define MOE_COMBINE(KK)                                                                   \
   do {                                                                                    \
-    if (payload == 0)                                                                     \
-      hipLaunchKernelGGL(combine_bf16_kernel<KK>, dim3((unsigned)col_chunks, (unsigned)T), \
-                         dim3(kBlock), 0, st, reinterpret_cast<const uint4*>(y), token_row, \
-                         w, reinterpret_cast<uint4*>(out), H, k);                          \
+    if (payload == 0 && ds)                                                               \
+      hipLaunchKernelGGL((combine_bf16_kernel<KK, true>),                                  \
+                         dim3((unsigned)col_chunks, (unsigned)T), dim3(kBlock), 0, st,      \
+                         reinterpret_cast<const uint4*>(y), token_row, w,                 \
+                         reinterpret_cast<uint4*>(out), H, k);                             \
+    else if (payload == 0)                                                                \
+      hipLaunchKernelGGL((combine_bf16_kernel<KK, false>),                                 \
+                         dim3((unsigned)col_chunks, (unsigned)T), dim3(kBlock), 0, st,      \
+                         reinterpret_cast<const uint4*>(y), token_row, w,                 \
+                         reinterpret_cast<uint4*>(out), H, k);                             \
     else                                                                                  \
       hipLaunchKernelGGL(combine_fp8_kernel<KK>, dim3(blocks), dim3(kBlock), 0, st,       \
                          reinterpret_cast<const uint2*>(y), ys, token_row, w,             \
