@@ -378,13 +378,15 @@ def stream_floor(torch, stream, time_graph, nbytes, n):
     write of `nbytes` with 16-byte accesses, and an empty launch, timed like
     the kernels (graphs of n launches over rotating buffers, cold).  Read: a
     non-temporal grid-stride loop, the best of three grid sizes.  Write: the
-    best of that loop and of 64 KB blocks stored with each cache policy."""
+    best of that loop and of 64 KB blocks stored with each cache policy.
+    Copy: read and write of `nbytes` each, the non-temporal loop."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "combine_moe_dispatch_amd", "libmoe_ceiling.so"))
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     lib.moe_ceiling_read.argtypes = [vp, sz, vp, i32, vp]
     lib.moe_ceiling_write.argtypes = [vp, sz, i32, vp]
     lib.moe_ceiling_write_blocked.argtypes = [vp, sz, i32, vp]
+    lib.moe_ceiling_copy.argtypes = [vp, vp, sz, i32, vp]
     lib.moe_ceiling_empty.argtypes = [vp]
     nbytes = (nbytes + 15) // 16 * 16
     S = min(64, max(2, math.ceil(2 * MALL_BYTES / nbytes)))
@@ -416,10 +418,14 @@ def stream_floor(torch, stream, time_graph, nbytes, n):
     wr = min([wr] + [timed(lambda i, c=c: lib.moe_ceiling_write_blocked(bufs[i % S].data_ptr(),
                                                                        nvec, c, st))
                      for c in (0, 1, 2)])
+    # copy: read one buffer, write the next (both rotate)
+    cp = min(timed(lambda i, b=b: lib.moe_ceiling_copy(bufs[i % S].data_ptr(),
+                                                       bufs[(i + 1) % S].data_ptr(), nvec, b, st))
+             for b in grids)
     em = timed(lambda i: lib.moe_ceiling_empty(st))
     del bufs
     torch.cuda.empty_cache()
-    return {"bytes": nbytes, "read_us": rd, "write_us": wr, "empty_launch_us": em}
+    return {"bytes": nbytes, "read_us": rd, "write_us": wr, "copy_us": cp, "empty_launch_us": em}
 
 
 def cpu_baseline(w, inp, seconds):
@@ -591,7 +597,8 @@ def main():
         fl = g["floor"]
         line["stream_floor"] = {
             "payload_bytes": fl["bytes"], "read_us": round(fl["read_us"], 3),
-            "write_us": round(fl["write_us"], 3), "empty_launch_us": round(fl["empty_launch_us"], 3),
+            "write_us": round(fl["write_us"], 3), "copy_us": round(fl["copy_us"], 3),
+            "empty_launch_us": round(fl["empty_launch_us"], 3),
             "read_GBps": round(fl["bytes"] / (fl["read_us"] * 1e-6) / 1e9, 1),
             "write_GBps": round(fl["bytes"] / (fl["write_us"] * 1e-6) / 1e9, 1),
             "dispatch_over_write_floor": round(cold["dispatch_us"] / fl["write_us"], 3),

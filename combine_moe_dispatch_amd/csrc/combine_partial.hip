@@ -167,17 +167,15 @@ combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ 
                                     : make_uint4(0, 0, 0, 0);
   }
   // group of slot g = index of its rank among the token's distinct ranks in
-  // ascending order; m = number of distinct ranks
+  // ascending order
   bool first[kGroup];  // slot g is the first slot of its rank
   int grp[kGroup];
-  int m = 0;
 #pragma unroll
   for (int g = 0; g < kGroup; ++g) {
     bool f = rank[g] >= 0;
 #pragma unroll
     for (int g2 = 0; g2 < g; ++g2) f = f & (rank[g2] != rank[g]);
     first[g] = f;
-    m += f ? 1 : 0;
   }
 #pragma unroll
   for (int g = 0; g < kGroup; ++g) {
@@ -193,13 +191,17 @@ combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ 
     partial_rank[(size_t)t * M + lane] = r;
   }
   if (!active) return;
-  for (int q = 0; q < m; ++q) {
+  // each group once, from its first slot: that slot and the later slots of
+  // the same rank are folded in slot order, then the row is stored
+#pragma unroll
+  for (int g0 = 0; g0 < kGroup; ++g0) {
+    if (!first[g0]) continue;
     float acc[8 * KV];
 #pragma unroll
     for (int c = 0; c < 8 * KV; ++c) acc[c] = 0.0f;
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      if (grp[g] != q) continue;
+    for (int g = g0; g < kGroup; ++g) {
+      if (g > g0 && rank[g] != rank[g0]) continue;
       float val[8 * KV];
       if constexpr (FP8) {
 #pragma unroll
@@ -220,7 +222,7 @@ combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ 
 #pragma unroll
       for (int c = 0; c < 8 * KV; ++c) acc[c] = fmaf(wj[g], val[c], acc[c]);
     }
-    uint4* dst = partial + ((size_t)t * M + q) * nv;
+    uint4* dst = partial + ((size_t)t * M + grp[g0]) * nv;
 #pragma unroll
     for (int i = 0; i < KV; ++i)
       if (u[i] < nv) store_partial<8>(&dst[u[i]], &acc[8 * i]);
