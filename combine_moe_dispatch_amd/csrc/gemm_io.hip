@@ -149,10 +149,11 @@ hipError_t launch_gemm_io(bool pack, const void* src, const float* src_scales, v
                           int payload, hipStream_t st) {
   const int row_bytes = payload == 0 ? 2 * H : H;
   const int nb = payload == 0 ? 0 : H / kFp8Block;
-  // one dense row per wave up to 8192 rows, then 4 (every wave loads all E
-  // counts and offsets: a few KB from L2)
-  const int R = max_rows <= 8192 ? 1 : 4;
-  const dim3 grid((unsigned)max(1, (max_rows + R - 1) / R));
+  // one dense row per wave: every wave loads all E counts and offsets (a few
+  // KB, from L2), which costs less than moving several rows one after the
+  // other in a wave (measured at 32768 rows: 156 us against 178 with 4)
+  const int R = 1;
+  const dim3 grid((unsigned)max(1, max_rows));
   const uint32_t l_magic = L >= 2 ? (uint32_t)(((1ull << 32) + L - 1) / L) : 0u;
   const uint8_t* s = reinterpret_cast<const uint8_t*>(src);
   uint8_t* d = reinterpret_cast<uint8_t*>(dst);
