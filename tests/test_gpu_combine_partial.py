@@ -27,6 +27,7 @@ pytestmark = pytest.mark.gpu
     (100, 256, 16, 4, 4, 60, 0, True),         # capacity-skipped pairs
     (50, 536, 64, 8, 8, 0, 0, False),          # ragged row: last chunk has 3 live lanes < k
     (0, 256, 16, 4, 4, 0, 0, False),           # no tokens
+    (2400, 7168, 256, 8, 32, 0, 0, False),     # 34 MB output: device-scope stores
 ])
 def test_two_stage_combine(T, H, E, k, N, C, payload, skew):
     print(f"[case] two-stage T={T} H={H} E={E} k={k} N={N} C={C} p={payload}", flush=True)
