@@ -142,6 +142,12 @@ __device__ __forceinline__ uint64_t wave_match(uint32_t key, int bits) {
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
+// Kernel arguments are scalar loads, and the compiler issues them where they
+// are first needed: behind an early branch they come one memory round trip
+// later.  An empty asm that reads the values from scalar registers before
+// the branch makes them part of the first batch of argument loads.
+#define MOE_ARGS_UP_FRONT(...) asm volatile("" ::__VA_ARGS__)
+
 // n / d without a division, for any n < 2^32 and d >= 1: with
 // m = floor((2^32 - 1) / d), umulhi(n, m) is floor(n / d) or one less (the
 // product undershoots n / d by less than n / 2^32 < 1), and one remainder

@@ -123,6 +123,7 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int t = blockIdx.x * kRouteWaves + wave;
+  MOE_ARGS_UP_FRONT("s"(logits), "s"(bias));  // fetched with T
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
 
