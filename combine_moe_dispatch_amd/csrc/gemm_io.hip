@@ -27,14 +27,14 @@ namespace moe {
 namespace {
 
 // PACK: receive regions -> dense rows; otherwise dense rows -> regions.
-// Block b moves dense rows [b*R, b*R + R).
+// Block b moves dense row b.
 template <bool PACK, int PER, int KV>
 __global__ void __launch_bounds__(kWave)
 gemm_io_kernel(const uint8_t* __restrict__ src, const float* __restrict__ src_scales,
                uint8_t* __restrict__ dst, float* __restrict__ dst_scales,
                const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
                int32_t* __restrict__ dense_out, int E, int C, uint32_t l_magic, int row_bytes,
-               int nb, int R) {
+               int nb) {
   const int lane = threadIdx.x;
   const int e0 = lane * PER;
   int cnt[PER], off[PER];
@@ -78,65 +78,64 @@ gemm_io_kernel(const uint8_t* __restrict__ src, const float* __restrict__ src_sc
     if (lane == 0) dense_out[E] = total;
   }
   const int nvec = row_bytes / 16;
-  const int i_end = min(total, (int)(blockIdx.x + 1) * R);
-  for (int i = blockIdx.x * R; i < i_end; ++i) {
-    // the one expert segment holding dense row i
-    int hit = -1;
+  const int i = blockIdx.x;
+  if (i >= total) return;
+  // the one expert segment holding dense row i
+  int hit = -1;
 #pragma unroll
-    for (int q = 0; q < PER; ++q)
-      if (dense[q] <= i && i < dense[q] + placed[q]) hit = off[q] + (i - dense[q]);
-    const uint64_t m = __ballot(hit >= 0);
-    if (m == 0) continue;  // not reached: i < total lies in some segment
-    const int region_row = __builtin_amdgcn_readlane(hit, (int)__builtin_ctzll(m));
-    const size_t from = PACK ? (size_t)region_row : (size_t)i;
-    const size_t to = PACK ? (size_t)i : (size_t)region_row;
-    const uint4* s4 = reinterpret_cast<const uint4*>(src + from * row_bytes);
-    uint4* d4 = reinterpret_cast<uint4*>(dst + to * row_bytes);
-    for (int v0 = 0; v0 < nvec; v0 += KV * kWave) {
-      uint4 buf[KV];
+  for (int q = 0; q < PER; ++q)
+    if (dense[q] <= i && i < dense[q] + placed[q]) hit = off[q] + (i - dense[q]);
+  const uint64_t m = __ballot(hit >= 0);
+  if (m == 0) return;  // not reached: i < total lies in some segment
+  const int region_row = __builtin_amdgcn_readlane(hit, (int)__builtin_ctzll(m));
+  const size_t from = PACK ? (size_t)region_row : (size_t)i;
+  const size_t to = PACK ? (size_t)i : (size_t)region_row;
+  const uint4* s4 = reinterpret_cast<const uint4*>(src + from * row_bytes);
+  uint4* d4 = reinterpret_cast<uint4*>(dst + to * row_bytes);
+  for (int v0 = 0; v0 < nvec; v0 += KV * kWave) {
+    uint4 buf[KV];
 #pragma unroll
-      for (int j = 0; j < KV; ++j) buf[j] = load_stream(&s4[min(v0 + j * kWave + lane, nvec - 1)]);
+    for (int j = 0; j < KV; ++j) buf[j] = load_stream(&s4[min(v0 + j * kWave + lane, nvec - 1)]);
 #pragma unroll
-      for (int j = 0; j < KV; ++j) {
-        const int v = v0 + j * kWave + lane;
-        if (v < nvec) store_stream(&d4[v], buf[j]);
-      }
+    for (int j = 0; j < KV; ++j) {
+      const int v = v0 + j * kWave + lane;
+      if (v < nvec) store_stream(&d4[v], buf[j]);
     }
-    if (src_scales)
-      for (int b = lane; b < nb; b += kWave) dst_scales[to * nb + b] = src_scales[from * nb + b];
   }
+  if (src_scales)
+    for (int b = lane; b < nb; b += kWave) dst_scales[to * nb + b] = src_scales[from * nb + b];
 }
 
 template <bool PACK, int PER>
 void launch_kv(int nvec, dim3 grid, hipStream_t st, const uint8_t* s, const float* ss,
                uint8_t* d, float* ds, const int32_t* counts, const int32_t* offsets,
-               int32_t* dense_out, int E, int C, uint32_t l_magic, int row_bytes, int nb, int R) {
+               int32_t* dense_out, int E, int C, uint32_t l_magic, int row_bytes, int nb) {
   // vectors per lane and pass: enough for a whole row where it fits in 16
   if (nvec <= 4 * kWave)
     hipLaunchKernelGGL((gemm_io_kernel<PACK, PER, 4>), grid, dim3(kWave), 0, st, s, ss, d, ds,
-                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb, R);
+                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb);
   else if (nvec <= 8 * kWave)
     hipLaunchKernelGGL((gemm_io_kernel<PACK, PER, 8>), grid, dim3(kWave), 0, st, s, ss, d, ds,
-                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb, R);
+                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb);
   else
     hipLaunchKernelGGL((gemm_io_kernel<PACK, PER, 16>), grid, dim3(kWave), 0, st, s, ss, d, ds,
-                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb, R);
+                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb);
 }
 
 template <bool PACK>
 void launch_per(int nvec, dim3 grid, hipStream_t st, const uint8_t* s, const float* ss,
                 uint8_t* d, float* ds, const int32_t* counts, const int32_t* offsets,
-                int32_t* dense_out, int E, int C, uint32_t l_magic, int row_bytes, int nb, int R) {
+                int32_t* dense_out, int E, int C, uint32_t l_magic, int row_bytes, int nb) {
   // experts per lane: E <= 64 * PER
   if (E <= 4 * kWave)
     launch_kv<PACK, 4>(nvec, grid, st, s, ss, d, ds, counts, offsets, dense_out, E, C, l_magic,
-                       row_bytes, nb, R);
+                       row_bytes, nb);
   else if (E <= 8 * kWave)
     launch_kv<PACK, 8>(nvec, grid, st, s, ss, d, ds, counts, offsets, dense_out, E, C, l_magic,
-                       row_bytes, nb, R);
+                       row_bytes, nb);
   else
     launch_kv<PACK, 16>(nvec, grid, st, s, ss, d, ds, counts, offsets, dense_out, E, C, l_magic,
-                        row_bytes, nb, R);
+                        row_bytes, nb);
 }
 
 static_assert(kMaxExperts <= 16 * kWave, "the widest kernel holds 16 experts per lane");
@@ -152,7 +151,6 @@ hipError_t launch_gemm_io(bool pack, const void* src, const float* src_scales, v
   // one dense row per wave: every wave loads all E counts and offsets (a few
   // KB, from L2), which costs less than moving several rows one after the
   // other in a wave (measured at 32768 rows: 156 us against 178 with 4)
-  const int R = 1;
   const dim3 grid((unsigned)max(1, max_rows));
   const uint32_t l_magic = L >= 2 ? (uint32_t)(((1ull << 32) + L - 1) / L) : 0u;
   const uint8_t* s = reinterpret_cast<const uint8_t*>(src);
@@ -161,10 +159,10 @@ hipError_t launch_gemm_io(bool pack, const void* src, const float* src_scales, v
   const int nvec = row_bytes / 16;
   if (pack)
     launch_per<true>(nvec, grid, st, s, ss, d, dst_scales, counts, offsets, dense_out, E, C,
-                     l_magic, row_bytes, nb, R);
+                     l_magic, row_bytes, nb);
   else
     launch_per<false>(nvec, grid, st, s, ss, d, dst_scales, counts, offsets, dense_out, E, C,
-                      l_magic, row_bytes, nb, R);
+                      l_magic, row_bytes, nb);
   return hipGetLastError();
 }
 
