@@ -22,10 +22,6 @@ namespace {
 constexpr int kBlock = 64;  // one wavefront per block
 constexpr int kGroup = 8;   // gathers in flight per thread
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
-
 // Fold n gathered rows into acc with fp32 fused multiply-adds in slot order.
 template <int N>
 __device__ __forceinline__ void fold_rows(float (&acc)[8], const uint4 (&yv)[N],

@@ -27,10 +27,6 @@ namespace {
 constexpr int kBlock = 64;  // one wavefront per block
 constexpr int kGroup = 8;   // row loads in flight per thread
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
-
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
@@ -191,6 +187,11 @@ combine_send_small_kernel(const void* __restrict__ y, const float* __restrict__ 
     partial_rank[(size_t)t * M + lane] = r;
   }
   if (!active) return;
+  // wait here for every gather, on every path: the folds below sit behind
+  // uniform branches, and without this the compiler places a full vmcnt wait
+  // before each of them, which on this GPU also waits for the partial rows
+  // already being stored (stores count in vmcnt too)
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   // each group once, from its first slot: that slot and the later slots of
   // the same rank are folded in slot order, then the row is stored
 #pragma unroll

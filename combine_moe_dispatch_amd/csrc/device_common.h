@@ -13,13 +13,17 @@ constexpr int kMaxExperts = 1024;  // LDS histograms are sized for this
 constexpr int kMaxTopK = 32;
 constexpr int kFp8Block = 128;     // columns per fp8 scale
 
-// bf16 (8 exponent bits, 7 mantissa bits) from fp32, round to nearest even.
-// NaN stays NaN (quiet).  Pure integer arithmetic on the bit pattern.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float v) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 values to a bf16 pair (lo in bits 15:0; bf16 = 8 exponent bits,
+// 7 mantissa bits) with the gfx950 packed convert in one instruction: round
+// to nearest even on the bit pattern, NaN quieted (the 0x0040 bit set), which
+// equals the integer rounding u + 0x7fff + ((u >> 16) & 1), then >> 16, for
+// every one of the 2^32 fp32 patterns (checked exhaustively on the GPU, in
+// both halves).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
@@ -141,6 +145,11 @@ __device__ __forceinline__ uint64_t wave_match(uint32_t key, int bits) {
 }
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+
+// s_waitcnt operand that waits for vmcnt == 0 and leaves expcnt (7) and
+// lgkmcnt (15) unconstrained (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt in 6:4, lgkmcnt in 11:8).
+constexpr unsigned kWaitVm0 = 0x0F70;
 
 // Kernel arguments are scalar loads, and the compiler issues them where they
 // are first needed: behind an early branch they come one memory round trip

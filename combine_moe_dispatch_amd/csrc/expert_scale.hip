@@ -42,7 +42,7 @@ expert_scale_bf16_kernel(const uint4* recv, const int32_t* counts, const int32_t
       for (int m = 0; m < 4; ++m) {
         const float lo = a * bf16_lo(q[m]);
         const float hi = a * bf16_hi(q[m]);
-        o[m] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+        o[m] = pack_bf16x2(lo, hi);
       }
       y[(size_t)row * nvec + v] = make_uint4(o[0], o[1], o[2], o[3]);
     }
