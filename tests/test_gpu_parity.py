@@ -76,6 +76,8 @@ SWEEP = [
     # (k <= 8) and by the readlane loop (k > 8)
     (256, 512, 32, 8, 4, 2048, 0, False, 5),       # L = 8
     (120, 256, 96, 8, 4, 960, 0, False, 2),        # L = 24
+    (200, 512, 64, 8, 4, 800, 0, False, 3),        # L = 16: four 16-byte reads
+    (150, 256, 48, 8, 4, 600, 1, True, None),      # L = 12, fp8
     (50, 256, 30, 4, 5, 200, 0, False, None),      # L = 6
     (100, 512, 64, 12, 8, 800, 1, False, 3),       # k = 12, fp8
     (100, 512, 64, 6, 8, 600, 0, True, None),      # k = 6 (compile-time combine)
