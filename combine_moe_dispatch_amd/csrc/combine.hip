@@ -7,11 +7,13 @@
 // chunk); the token's k rows and weights are read at uniform addresses (no
 // LDS staging, no barrier), each thread issues its k 16-byte gathers together
 // (8 at a time) and folds them with fp32 fused multiply-adds in slot order
-// from zero, then rounds to bf16 (nearest even) and stores 16 bytes.  The
-// gathers and the stores carry non-temporal (streaming) hints.  With
-// the fp8 payload a thread owns 16 columns: two 8-byte gathers of codes per
-// row, each code decoded exactly to fp32 (the hardware OCP e4m3 convert) and
-// multiplied by its block's fp32 scale.  This is a bandwidth-bound gather-reduce: no MFMA.
+// from zero, then rounds to bf16 (nearest even, the hardware packed convert)
+// and stores 16 bytes.  The gathers carry non-temporal (streaming) hints, and
+// so do the stores of outputs below 32 MB (larger ones are stored with device
+// scope).  With the fp8 payload a thread owns 16 columns: two 8-byte gathers
+// of codes per row, each code decoded exactly to fp32 (the hardware OCP e4m3
+// convert) and multiplied by its block's fp32 scale.  This is a
+// bandwidth-bound gather-reduce: no MFMA.
 #include "device_common.h"
 #include "launch.h"
 

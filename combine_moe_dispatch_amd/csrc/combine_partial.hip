@@ -12,11 +12,13 @@
 // Stage 2 (recv): out[t] = bf16(fp32 sum of the used partial rows in slot
 // order from 0).
 //
-// A one-wave block owns (token, 64-vector column chunk).  Lane j holds slot
-// j's row, rank and weight; the rank grouping is a few readlanes.  With
-// k <= 8 all k rows are loaded at once and the groups are folded and stored
-// one after the other; with larger k rows stream in 8 at a time and are
-// folded into up to GC group accumulators (more groups take more passes).
+// A one-wave block owns (token, 64-vector column chunk).  With k <= 8 the
+// slots' rows, ranks and weights are uniform scalar loads and the grouping is
+// scalar arithmetic; all k rows are loaded at once and each group is folded
+// once, from its first slot, and stored.  With larger k lane j holds slot j's
+// row, rank and weight (the grouping is a few readlanes), and rows stream in
+// 8 at a time, folded into up to GC group accumulators (more groups take more
+// passes).  bf16 rounding is the hardware packed convert.
 #include "device_common.h"
 #include "launch.h"
 
