@@ -6,12 +6,14 @@
 // with Multi-Node DeepSeek Deployment", MoE Router).
 //
 // Each lane holds ceil(E/64) biased logits (coalesced: value i of lane l is
-// expert i*64 + l) and sorts them once, best first, by (value descending, id
-// ascending).  Each of the k rounds then takes every lane's head, finds the
-// wave's best (value, id) with a DPP butterfly inside each 16-lane row and two
-// DPP row broadcasts across the rows, and the owning lane pops its head.  Equal
-// values go to the lower expert id, so slots come out in descending order.
-// Lanes 0..k-1 then form the weights in fp32 and normalise them to one.
+// expert i*64 + l), packs each with its id into one 64-bit key whose unsigned
+// order is (value descending, id ascending), and sorts its keys once, best
+// first.  Each of the k rounds then takes every lane's head, finds the wave's
+// largest key with a DPP butterfly inside each 16-lane row and two DPP row
+// broadcasts across the rows (one 64-bit compare per step), and the owning
+// lane pops its head.  Equal values go to the lower expert id, so slots come
+// out in descending order.  Lanes 0..k-1 then form the weights in fp32 and
+// normalise them to one.
 //
 // Group-limited routing (same page, MoE Router: plain top-k is the case where
 // the kept groups are all experts): the wave stages its biased logits in LDS,
@@ -72,6 +74,47 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   dpp_max_step_rows<0x143, 0xc>(v, i);  // row_bcast:31 into rows 2 and 3
   v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
   i = __builtin_amdgcn_readlane(i, 63);
+}
+
+// (value, id) as one 64-bit key whose unsigned order is the selection order:
+// the high word maps the fp32 value to an order-preserving unsigned (sign bit
+// flipped for non-negative values, all bits for negative ones; -0 is taken
+// as +0 first, as the float comparison does), the low word is the bitwise
+// complement of the id, so of two equal values the lower id has the larger
+// key.  An absent entry is key 0, below every real one.
+__device__ __forceinline__ uint64_t route_key(float v, int id) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)id;
+}
+__device__ __forceinline__ float route_key_value(uint64_t key) {
+  const uint32_t u = (uint32_t)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+__device__ __forceinline__ int route_key_id(uint64_t key) { return (int)~(uint32_t)key; }
+
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ void dpp_key_max(uint64_t& key) {
+  const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
+  const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWMASK, 0xf, false);
+  const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWMASK, 0xf, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  key = o > key ? o : key;
+}
+
+// Largest key over the wave (uniform result): the same butterfly and row
+// broadcasts as wave_argmax, on 64-bit keys.
+__device__ __forceinline__ uint64_t wave_key_max(uint64_t key) {
+  dpp_key_max<0xB1, 0xf>(key);
+  dpp_key_max<0x4E, 0xf>(key);
+  dpp_key_max<0x141, 0xf>(key);
+  dpp_key_max<0x140, 0xf>(key);
+  dpp_key_max<0x142, 0xa>(key);
+  dpp_key_max<0x143, 0xc>(key);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)key, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(key >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Keep the two largest values seen (equal values fill both).
@@ -242,42 +285,33 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
       }
     }
   }
-  // sort this lane's entries, best first (insertion network, fully unrolled)
+  // this lane's entries as keys, sorted best first (insertion network)
+  uint64_t key[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) key[i] = id[i] == kNone ? 0ull : route_key(v[i], id[i]);
 #pragma unroll
   for (int a = 1; a < VPL; ++a) {
 #pragma unroll
     for (int b = a; b > 0; --b) {
-      if (better(v[b], id[b], v[b - 1], id[b - 1])) {
-        const float tv = v[b];
-        v[b] = v[b - 1];
-        v[b - 1] = tv;
-        const int ti = id[b];
-        id[b] = id[b - 1];
-        id[b - 1] = ti;
-      }
+      const uint64_t hi = key[b] > key[b - 1] ? key[b] : key[b - 1];
+      const uint64_t lo = key[b] > key[b - 1] ? key[b - 1] : key[b];
+      key[b - 1] = hi;
+      key[b] = lo;
     }
   }
 
-  float my_val = 0.0f;  // lane j keeps the biased logit and id of slot j
-  int my_id = 0;
+  uint64_t my_key = 0;  // lane j keeps the key of slot j
   for (int j = 0; j < k; ++j) {
-    float bv = v[0];
-    int bi = id[0];
-    wave_argmax(bv, bi);
-    if (bi == id[0]) {  // this lane owned the winner: pop its head
+    const uint64_t best = wave_key_max(key[0]);
+    if (best == key[0]) {  // this lane owned the winner: pop its head
 #pragma unroll
-      for (int i = 0; i + 1 < VPL; ++i) {
-        v[i] = v[i + 1];
-        id[i] = id[i + 1];
-      }
-      v[VPL - 1] = -INFINITY;
-      id[VPL - 1] = kNone;
+      for (int i = 0; i + 1 < VPL; ++i) key[i] = key[i + 1];
+      key[VPL - 1] = 0ull;
     }
-    if (lane == j) {
-      my_val = bv;
-      my_id = bi;
-    }
+    if (lane == j) my_key = best;
   }
+  const float my_val = route_key_value(my_key);
+  const int my_id = route_key_id(my_key);
 
   float s = 0.0f;
   const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));

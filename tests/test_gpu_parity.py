@@ -155,6 +155,21 @@ def test_route_softmax_and_ties():
         np.testing.assert_allclose(w.cpu().numpy(), o_w, rtol=2.0 ** -20, atol=0)
 
 
+def test_route_signed_zero_logits():
+    """-0 and +0 are equal logits: ties go to the lower id, as the float
+    comparison has it (the selection keys treat -0 as +0)."""
+    _announce("route signed zeros")
+    T, E, k = 64, 256, 8
+    rng = np.random.default_rng(11)
+    logits = rng.choice(np.array([0.0, -0.0, -0.0, 0.0, -1.0, -0.5], np.float32),
+                        size=(T, E)).astype(np.float32)
+    for score in (api.MOE_SCORE_SOFTMAX, api.MOE_SCORE_SIGMOID):
+        ids, _ = api.moe_route_topk(torch.from_numpy(logits).cuda(), None, k, score)
+        torch.cuda.synchronize()
+        o_ids, _ = oracle.route_topk(logits, None, k, score)
+        assert np.array_equal(ids.cpu().numpy(), o_ids)
+
+
 def test_graph_capture_replays_match_eager():
     """route -> dispatch -> combine captured once and replayed several times,
     with eager work between replays; every replay equals the eager result."""
