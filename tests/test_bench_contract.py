@@ -75,3 +75,21 @@ def test_bench_prints_one_contract_line():
     assert nx["combine_partial"]["send_us"] > 0 and nx["combine_partial"]["recv_us"] > 0
     assert nx["split"]["dispatch_recv_us"] > 0 and nx["split"]["combine_send_us"] > 0
     assert nx["route_grouped"]["route_us"] > 0
+
+
+@pytest.mark.gpu
+def test_bench_flag_paths_run():
+    """The two-stage combine, the split timing and the group-limited router
+    as the main path of a bench run (tiny workload)."""
+    print("[case] bench.py tiny workload with --combine two-stage --split --groups 4", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny",
+                        "--steps", "5", "--warmup", "1", "--no-cpu-baseline", "--no-warm",
+                        "--no-floor", "--combine", "two-stage", "--split", "--groups", "4",
+                        "--topk-groups", "2"],
+                       capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads([l for l in r.stdout.splitlines() if l.strip()][-1])
+    assert d["config"]["combine"].startswith("sender-side")
+    assert d["config"]["router"].startswith("group-limited")
+    assert d["two_stage_combine"]["send_us"] > 0 and d["split"]["dispatch_recv_us"] > 0
+    assert d["device_status"] == 0
