@@ -13,7 +13,8 @@
 // the calls need no host round trip and can be captured in a graph.
 //
 // One wave per block, no LDS and no barrier: every wave loads all experts'
-// counts and segment offsets (PER consecutive experts per lane), forms the
+// counts and segment offsets (PER consecutive experts per lane, as 16-byte
+// loads where E is a multiple of 4), forms the
 // dense offsets with a DPP scan, and finds the expert of each of its dense
 // rows by a compare in every lane and a ballot.  Wave 0 publishes the dense
 // offsets.  A row then moves as 16-byte streaming accesses, all loads of a
@@ -34,15 +35,29 @@ gemm_io_kernel(const uint8_t* __restrict__ src, const float* __restrict__ src_sc
                uint8_t* __restrict__ dst, float* __restrict__ dst_scales,
                const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
                int32_t* __restrict__ dense_out, int E, int C, uint32_t l_magic, int row_bytes,
-               int nb) {
+               int nb, int vec4) {
   const int lane = threadIdx.x;
   const int e0 = lane * PER;
   int cnt[PER], off[PER];
+  // every load first (clamped): one round trip.  vec4 (E % 4 == 0, both
+  // arrays 16-byte aligned): a lane's PER consecutive entries as 16-byte loads
+  if (PER % 4 == 0 && vec4) {
+    const int4* c4 = reinterpret_cast<const int4*>(counts);
+    const int4* o4 = reinterpret_cast<const int4*>(offsets);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {  // every load first (clamped): one round trip
-    const int e = min(e0 + i, E - 1);
-    cnt[i] = counts[e];
-    off[i] = offsets[e];
+    for (int i = 0; i < PER / 4; ++i) {
+      const int vi = min(lane * (PER / 4) + i, E / 4 - 1);
+      const int4 c = c4[vi], o = o4[vi];
+      cnt[4 * i] = c.x; cnt[4 * i + 1] = c.y; cnt[4 * i + 2] = c.z; cnt[4 * i + 3] = c.w;
+      off[4 * i] = o.x; off[4 * i + 1] = o.y; off[4 * i + 2] = o.z; off[4 * i + 3] = o.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = min(e0 + i, E - 1);
+      cnt[i] = counts[e];
+      off[i] = offsets[e];
+    }
   }
   // placed rows per expert: the count, cut at the end of the expert's rank
   // region for fixed capacity (rank = e / L by a multiply-high with
@@ -109,33 +124,35 @@ gemm_io_kernel(const uint8_t* __restrict__ src, const float* __restrict__ src_sc
 template <bool PACK, int PER>
 void launch_kv(int nvec, dim3 grid, hipStream_t st, const uint8_t* s, const float* ss,
                uint8_t* d, float* ds, const int32_t* counts, const int32_t* offsets,
-               int32_t* dense_out, int E, int C, uint32_t l_magic, int row_bytes, int nb) {
+               int32_t* dense_out, int E, int C, uint32_t l_magic, int row_bytes, int nb,
+               int vec4) {
   // vectors per lane and pass: enough for a whole row where it fits in 16
   if (nvec <= 4 * kWave)
     hipLaunchKernelGGL((gemm_io_kernel<PACK, PER, 4>), grid, dim3(kWave), 0, st, s, ss, d, ds,
-                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb);
+                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb, vec4);
   else if (nvec <= 8 * kWave)
     hipLaunchKernelGGL((gemm_io_kernel<PACK, PER, 8>), grid, dim3(kWave), 0, st, s, ss, d, ds,
-                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb);
+                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb, vec4);
   else
     hipLaunchKernelGGL((gemm_io_kernel<PACK, PER, 16>), grid, dim3(kWave), 0, st, s, ss, d, ds,
-                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb);
+                       counts, offsets, dense_out, E, C, l_magic, row_bytes, nb, vec4);
 }
 
 template <bool PACK>
 void launch_per(int nvec, dim3 grid, hipStream_t st, const uint8_t* s, const float* ss,
                 uint8_t* d, float* ds, const int32_t* counts, const int32_t* offsets,
-                int32_t* dense_out, int E, int C, uint32_t l_magic, int row_bytes, int nb) {
+                int32_t* dense_out, int E, int C, uint32_t l_magic, int row_bytes, int nb,
+               int vec4) {
   // experts per lane: E <= 64 * PER
   if (E <= 4 * kWave)
     launch_kv<PACK, 4>(nvec, grid, st, s, ss, d, ds, counts, offsets, dense_out, E, C, l_magic,
-                       row_bytes, nb);
+                       row_bytes, nb, vec4);
   else if (E <= 8 * kWave)
     launch_kv<PACK, 8>(nvec, grid, st, s, ss, d, ds, counts, offsets, dense_out, E, C, l_magic,
-                       row_bytes, nb);
+                       row_bytes, nb, vec4);
   else
     launch_kv<PACK, 16>(nvec, grid, st, s, ss, d, ds, counts, offsets, dense_out, E, C, l_magic,
-                        row_bytes, nb);
+                        row_bytes, nb, vec4);
 }
 
 static_assert(kMaxExperts <= 16 * kWave, "the widest kernel holds 16 experts per lane");
@@ -157,12 +174,14 @@ hipError_t launch_gemm_io(bool pack, const void* src, const float* src_scales, v
   uint8_t* d = reinterpret_cast<uint8_t*>(dst);
   const float* ss = payload ? src_scales : nullptr;
   const int nvec = row_bytes / 16;
+  const int vec4 = E % 4 == 0 && ((reinterpret_cast<uintptr_t>(counts) |
+                                   reinterpret_cast<uintptr_t>(offsets)) & 15) == 0;
   if (pack)
     launch_per<true>(nvec, grid, st, s, ss, d, dst_scales, counts, offsets, dense_out, E, C,
-                     l_magic, row_bytes, nb);
+                     l_magic, row_bytes, nb, vec4);
   else
     launch_per<false>(nvec, grid, st, s, ss, d, dst_scales, counts, offsets, dense_out, E, C,
-                      l_magic, row_bytes, nb);
+                      l_magic, row_bytes, nb, vec4);
   return hipGetLastError();
 }
 
