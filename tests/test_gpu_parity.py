@@ -84,6 +84,9 @@ SWEEP = [
     (100, 512, 64, 6, 8, 600, 1, False, 2),        # k = 6, fp8, repeats
     (64, 256, 256, 8, 2, 512, 0, False, 9),        # L = 128
     (2048, 512, 256, 32, 256, 0, 0, True, None),   # k at the library maximum
+    (64, 32768, 64, 4, 8, 0, 0, True, None),       # wide rows: 8 column chunks per token
+    (40, 16384, 32, 8, 4, 320, 1, True, None),     # wide fp8 rows, 128 scale blocks
+    (700, 20480, 64, 8, 8, 0, 0, False, 1),        # wide rows on the chunked path
 ]
 
 
