@@ -16,11 +16,15 @@
 // normalise them to one.
 //
 // Group-limited routing (same page, MoE Router: plain top-k is the case where
-// the kept groups are all experts): the wave stages its biased logits in LDS,
-// each group's score is the sum of its two largest logits (64/G lanes per
-// group merging pairs with DPP when G divides 64, else one lane per group),
-// topk_groups arg-max rounds keep the best groups (ties to the lower group
-// id), and the experts of the other groups drop out before the top-k rounds.
+// the kept groups are all experts): each group's score is the sum of its two
+// largest biased logits.  Where the groups fall on whole lanes (a lane then
+// holds ceil(E/64) consecutive experts, and a group a power-of-two block of
+// up to 16 lanes), every lane takes its own top two and DPP steps merge them
+// inside the group; otherwise the wave stages its logits in LDS and lane g
+// scans group g.  A group is kept when fewer than topk_groups groups beat it
+// (larger score, or equal score and lower id), counted with one 64-bit key
+// compare per group; the experts of the other groups drop out before the
+// top-k rounds.
 #include "device_common.h"
 #include "launch.h"
 
@@ -30,51 +34,6 @@ namespace {
 
 constexpr int kRouteWaves = 4;  // tokens per 256-thread block
 constexpr int kNone = 0x7fffffff;
-
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
-}
-
-// One butterfly step: exchange with the lane given by a DPP pattern.
-template <int CTRL>
-__device__ __forceinline__ void dpp_max_step(float& v, int& i) {
-  const float ov =
-      __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
-  const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xf, 0xf, false);
-  if (better(ov, oi, v, i)) {
-    v = ov;
-    i = oi;
-  }
-}
-
-// The same with a row mask: rows outside ROWMASK keep their own pair.
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ void dpp_max_step_rows(float& v, int& i) {
-  const float ov = __int_as_float(
-      __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWMASK, 0xf, false));
-  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROWMASK, 0xf, false);
-  if (better(ov, oi, v, i)) {
-    v = ov;
-    i = oi;
-  }
-}
-
-// Best (value, id) over the wave; the result is uniform.  Four butterfly
-// steps leave every lane of a 16-lane row with the row's best; the row
-// broadcasts then fold row 0 into row 1 and row 2 into row 3 (lane 15 of the
-// row before), and row 1 into rows 2-3 (lane 31), so lane 63 holds the wave's
-// best.  (better() is a strict order on distinct ids, so the order of folding
-// does not matter.)
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  dpp_max_step<0xB1>(v, i);   // quad_perm [1,0,3,2]: lane ^ 1
-  dpp_max_step<0x4E>(v, i);   // quad_perm [2,3,0,1]: lane ^ 2
-  dpp_max_step<0x141>(v, i);  // row_half_mirror: quad <-> neighbouring quad
-  dpp_max_step<0x140>(v, i);  // row_mirror: half-row <-> other half-row
-  dpp_max_step_rows<0x142, 0xa>(v, i);  // row_bcast:15 into rows 1 and 3
-  dpp_max_step_rows<0x143, 0xc>(v, i);  // row_bcast:31 into rows 2 and 3
-  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-  i = __builtin_amdgcn_readlane(i, 63);
-}
 
 // (value, id) as one 64-bit key whose unsigned order is the selection order:
 // the high word maps the fp32 value to an order-preserving unsigned (sign bit
@@ -103,8 +62,11 @@ __device__ __forceinline__ void dpp_key_max(uint64_t& key) {
   key = o > key ? o : key;
 }
 
-// Largest key over the wave (uniform result): the same butterfly and row
-// broadcasts as wave_argmax, on 64-bit keys.
+// Largest key over the wave (uniform result).  Four butterfly steps leave
+// every lane of a 16-lane row with the row's largest key; the row broadcasts
+// then fold row 0 into row 1 and row 2 into row 3 (lane 15 of the row
+// before), and row 1 into rows 2-3 (lane 31), so lane 63 holds the wave's
+// largest.  Keys are distinct, so the order of folding does not matter.
 __device__ __forceinline__ uint64_t wave_key_max(uint64_t key) {
   dpp_key_max<0xB1, 0xf>(key);
   dpp_key_max<0x4E, 0xf>(key);
@@ -161,126 +123,138 @@ template <int VPL, bool GROUPED>
 __global__ void __launch_bounds__(kRouteWaves * kWave)
 route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bias, int T,
                   int E, int k, int score, int n_groups, int topk_groups,
-                  int32_t* __restrict__ ids, float* __restrict__ weights) {
+                  int32_t* __restrict__ ids, float* __restrict__ weights, int lpg) {
   __shared__ __align__(16) float s_logit[GROUPED ? kRouteWaves : 1][GROUPED ? kMaxExperts : 1];
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int t = blockIdx.x * kRouteWaves + wave;
-  MOE_ARGS_UP_FRONT("s"(logits), "s"(bias));  // fetched with T
+  // fetched with T: everything the first loads and the group step need
+  if constexpr (GROUPED)
+    MOE_ARGS_UP_FRONT("s"(logits), "s"(bias), "s"(n_groups), "s"(topk_groups), "s"(lpg));
+  else
+    MOE_ARGS_UP_FRONT("s"(logits), "s"(bias));
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
 
+  // Group-limited routing on whole lanes (lpg > 0, set by the host): lane l
+  // holds the epl = ceil(E/64) consecutive experts from l*epl, and group g is
+  // the lpg aligned lanes from g*lpg (a power of two up to 16).  Otherwise
+  // (and for plain top-k) value i of lane l is expert i*64 + l.
+  const bool contig = GROUPED && lpg > 0;
+  const int epl = (int)((unsigned)(E + kWave - 1) >> 6);
+
   // every load is unconditional (index clamped, value masked below) and all
   // are issued before the first is used: one memory round trip
+  int eid[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) eid[i] = contig ? lane * epl + i : i * kWave + lane;
   float v[VPL], bv_[VPL];
   int id[VPL];
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) v[i] = row[min(i * kWave + lane, E - 1)];
+  for (int i = 0; i < VPL; ++i) v[i] = row[min(eid[i], E - 1)];
   if (bias) {
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) bv_[i] = bias[min(i * kWave + lane, E - 1)];
+    for (int i = 0; i < VPL; ++i) bv_[i] = bias[min(eid[i], E - 1)];
   } else {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) bv_[i] = 0.0f;
   }
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    const int e = i * kWave + lane;
-    const bool in = e < E;
+    const bool in = eid[i] < E && (!contig || i < epl);
     v[i] = in ? (bias ? v[i] + bv_[i] : v[i]) : -INFINITY;
-    id[i] = in ? e : kNone;
+    id[i] = in ? eid[i] : kNone;
   }
   if (GROUPED) {
-    float* sl = s_logit[wave];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (i * kWave + lane < E) sl[i * kWave + lane] = v[i];
-    wave_lds_sync();
     // group score = sum of the group's two largest biased logits
-    const int gsz = E / n_groups;
+    const int gsz = contig ? lpg * epl : E / n_groups;
     float gv = -INFINITY;
-    int gi = kNone;
-    const int lpg = kWave / n_groups;  // lanes per group, when n_groups divides 64
-    if (kWave % n_groups == 0 && lpg <= 16 && gsz % (4 * lpg) == 0 && gsz / lpg <= 16) {
-      // lpg lanes per group: each takes the top two of its gsz/lpg logits
-      // (16-byte LDS reads), then DPP steps inside the group's aligned lanes
-      // merge the pairs; the group's first lane holds the score
-      const int g = lane / lpg, part = lane % lpg, ipl = gsz / lpg;
-      const float4* g4 = reinterpret_cast<const float4*>(sl + g * gsz + part * ipl);
-      float q[16];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float4 f = 4 * c < ipl ? g4[c]
-                                     : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        q[4 * c] = f.x;
-        q[4 * c + 1] = f.y;
-        q[4 * c + 2] = f.z;
-        q[4 * c + 3] = f.w;
-      }
+    int lanes_per_group = 1;
+    if (contig) {
+      // the lane's own top two, then DPP merges inside the group's lanes;
+      // every lane of the group ends with the group's pair
       float m1 = -INFINITY, m2 = -INFINITY;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) top2_take(q[c], m1, m2);
+      for (int i = 0; i < VPL; ++i) top2_take(v[i], m1, m2);
       if (lpg >= 2) top2_merge<0xB1>(m1, m2);   // lane ^ 1
       if (lpg >= 4) top2_merge<0x4E>(m1, m2);   // lane ^ 2
       if (lpg >= 8) top2_merge<0x141>(m1, m2);  // mirrored quad
       if (lpg >= 16) top2_merge<0x140>(m1, m2); // mirrored half-row
-      if (part == 0) {
-        gv = gsz > 1 ? m1 + m2 : m1;
-        gi = g;
-      }
-    } else if (lane < n_groups) {
-      // lane g scans group g
-      float m1 = -INFINITY, m2 = -INFINITY;
-      if ((gsz & 3) == 0) {
-        // 16-byte LDS reads, 4 in flight per round
-        const float4* g4 = reinterpret_cast<const float4*>(sl + lane * gsz);
-        for (int c0 = 0; c0 < gsz / 4; c0 += 4) {
-          float q[16];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float4 f = c0 + c < gsz / 4 ? g4[c0 + c]
-                                              : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-            q[4 * c] = f.x;
-            q[4 * c + 1] = f.y;
-            q[4 * c + 2] = f.z;
-            q[4 * c + 3] = f.w;
-          }
-#pragma unroll
-          for (int c = 0; c < 16; ++c) top2_take(q[c], m1, m2);
-        }
-      } else {
-        for (int e = lane * gsz; e < lane * gsz + gsz; ++e) top2_take(sl[e], m1, m2);
-      }
       gv = gsz > 1 ? m1 + m2 : m1;
-      gi = lane;
-    }
-    // keep the topk_groups best groups
-    uint64_t kept = 0;
-    for (int r = 0; r < topk_groups; ++r) {
-      float bv = gv;
-      int bi = gi;
-      wave_argmax(bv, bi);
-      kept |= 1ull << bi;
-      if (bi == gi) {
-        gv = -INFINITY;
-        gi = kNone;
+      lanes_per_group = lpg;
+    } else {
+      // lane g scans group g in the wave's LDS copy of its biased logits
+      float* sl = s_logit[wave];
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (i * kWave + lane < E) sl[i * kWave + lane] = v[i];
+      wave_lds_sync();
+      if (lane < n_groups) {
+        float m1 = -INFINITY, m2 = -INFINITY;
+        if ((gsz & 3) == 0) {
+          // 16-byte LDS reads, 4 in flight per round
+          const float4* g4 = reinterpret_cast<const float4*>(sl + lane * gsz);
+          for (int c0 = 0; c0 < gsz / 4; c0 += 4) {
+            float q[16];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float4 f = c0 + c < gsz / 4
+                                   ? g4[c0 + c]
+                                   : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+              q[4 * c] = f.x;
+              q[4 * c + 1] = f.y;
+              q[4 * c + 2] = f.z;
+              q[4 * c + 3] = f.w;
+            }
+#pragma unroll
+            for (int c = 0; c < 16; ++c) top2_take(q[c], m1, m2);
+          }
+        } else {
+          for (int e = lane * gsz; e < lane * gsz + gsz; ++e) top2_take(sl[e], m1, m2);
+        }
+        gv = gsz > 1 ? m1 + m2 : m1;
       }
     }
-    if ((gsz & (gsz - 1)) == 0) {  // power-of-two groups: a shift, not a division
-      const int sh = __ffs(gsz) - 1;
+    // a group is kept when fewer than topk_groups groups beat it (larger
+    // score, or an equal score and a lower group id): one 64-bit key compare
+    // against each group's score, read from the group's first lane
+    const int my_g = lane >> (__ffs(lanes_per_group) - 1);
+    const uint64_t gkey = my_g < n_groups ? route_key(gv, my_g) : 0ull;
+    int beaten_by = 0;
+    for (int h = 0; h < n_groups; ++h) {
+      const int src = h * lanes_per_group;
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)gkey, src);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(gkey >> 32), src);
+      beaten_by += (((uint64_t)hi << 32) | lo) > gkey ? 1 : 0;
+    }
+    const bool keep = my_g < n_groups && beaten_by < topk_groups;
+    if (contig) {
+      // all of a lane's experts are in its own group
+      if (!keep) {
 #pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        if (id[i] != kNone && !((kept >> (id[i] >> sh)) & 1ull)) {
+        for (int i = 0; i < VPL; ++i) {
           v[i] = -INFINITY;
           id[i] = kNone;
         }
       }
     } else {
+      const uint64_t kept = __ballot(keep);  // bit g: group g (lane g) kept
+      if ((gsz & (gsz - 1)) == 0) {  // power-of-two groups: a shift, not a division
+        const int sh = __ffs(gsz) - 1;
 #pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        if (id[i] != kNone && !((kept >> (id[i] / gsz)) & 1ull)) {
-          v[i] = -INFINITY;
-          id[i] = kNone;
+        for (int i = 0; i < VPL; ++i) {
+          if (id[i] != kNone && !((kept >> (id[i] >> sh)) & 1ull)) {
+            v[i] = -INFINITY;
+            id[i] = kNone;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+          if (id[i] != kNone && !((kept >> (id[i] / gsz)) & 1ull)) {
+            v[i] = -INFINITY;
+            id[i] = kNone;
+          }
         }
       }
     }
@@ -335,12 +309,19 @@ hipError_t launch_vpl(const float* logits, const float* bias, int T, int E, int 
                       int score, int n_groups, int topk_groups, int32_t* ids, float* w,
                       hipStream_t st) {
   const int blocks = (T + kRouteWaves - 1) / kRouteWaves;
-  if (n_groups > 1 && topk_groups < n_groups)
+  if (n_groups > 1 && topk_groups < n_groups) {
+    // lanes per group when the groups fall on whole lanes, else 0
+    const int gsz = E / n_groups;
+    const int epl = (E + kWave - 1) / kWave;
+    const int lpg = gsz % epl == 0 ? gsz / epl : 0;
+    const bool on_lanes = lpg > 0 && lpg <= 16 && (lpg & (lpg - 1)) == 0;
     hipLaunchKernelGGL((route_topk_kernel<VPL, true>), dim3(blocks), dim3(kRouteWaves * kWave),
-                       0, st, logits, bias, T, E, k, score, n_groups, topk_groups, ids, w);
-  else
+                       0, st, logits, bias, T, E, k, score, n_groups, topk_groups,
+                       ids, w, on_lanes ? lpg : 0);
+  } else {
     hipLaunchKernelGGL((route_topk_kernel<VPL, false>), dim3(blocks), dim3(kRouteWaves * kWave),
-                       0, st, logits, bias, T, E, k, score, 1, 1, ids, w);
+                       0, st, logits, bias, T, E, k, score, 1, 1, ids, w, 0);
+  }
   return hipGetLastError();
 }
 

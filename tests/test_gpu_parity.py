@@ -280,6 +280,13 @@ def test_fp8_quantiser_at_extreme_magnitudes(T, k, payload_path):
     (100, 256, 32, 6, 8, 0.0, False),  # 2 lanes per group
     (100, 512, 8, 3, 8, 0.0, False),   # 8 lanes per group, 8 logits per lane
     (50, 256, 1, 1, 8, 0.0, False),    # one group: plain top-k
+    (90, 320, 8, 3, 8, 0.0, True),     # 5 experts per lane, 8 lanes per group
+    (70, 96, 3, 2, 6, 0.0, False),     # 3 groups of 16 lanes, lanes 48-63 empty
+    (30, 1024, 16, 6, 8, 0.0, True),   # 16 experts per lane, 4 lanes per group
+    # groups that do not fall on whole lanes: LDS copy, one lane per group
+    (100, 160, 8, 3, 8, 0.0, True),    # 20 experts per group, 3 per lane
+    (80, 120, 8, 3, 6, 0.0, False),    # 15 experts per group (scalar LDS reads)
+    (60, 256, 2, 1, 8, 0.0, True),     # 32 lanes per group
 ])
 def test_grouped_route(T, E, G, TG, k, zipf, ties):
     _announce(f"grouped route T={T} E={E} G={G} TG={TG} k={k}")
