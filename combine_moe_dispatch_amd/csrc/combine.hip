@@ -6,8 +6,9 @@
 // Buffers, Evaluation).  A one-wave block owns one (token, 64-vector column
 // chunk); the token's k rows and weights are read at uniform addresses (no
 // LDS staging, no barrier), each thread issues its k 16-byte gathers together
-// (8 at a time) and folds them with fp32 fused multiply-adds in slot order
-// from zero, then rounds to bf16 (nearest even, the hardware packed convert)
+// (8 at a time, unconditionally, so each row's fold waits for that row only)
+// and folds them with fp32 fused multiply-adds in slot order from zero, then
+// rounds to bf16 (nearest even, the hardware packed convert)
 // and stores 16 bytes.  The gathers carry non-temporal (streaming) hints, and
 // so do the stores of outputs below 32 MB (larger ones are stored with device
 // scope).  With the fp8 payload a thread owns 16 columns: two 8-byte gathers
@@ -56,8 +57,9 @@ combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ tok
   const int v = blockIdx.x * kBlock + threadIdx.x;
   const int32_t* trow = token_row + (size_t)t * k;
   const float* tw = w + (size_t)t * k;
-  // no early exit before the gathers: lanes past the row end only mask
-  // their accesses, so nothing delays the uniform loads of the token's rows
+  // no early exit before the gathers: lanes past the row end gather a
+  // clamped column and skip the store, so nothing delays the uniform loads
+  // of the token's rows
   const bool active = v < nvec;
   float acc[8];
 #pragma unroll
@@ -70,12 +72,20 @@ combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ tok
       row[g] = j0 + g < k ? trow[j0 + g] : -1;
       wj[g] = j0 + g < k ? tw[j0 + g] : 0.0f;
     }
+    // the gathers are unconditional (row and column clamped; a skipped row is
+    // left out of the fold), so the fold of each row waits for that row only
     uint4 yv[kGroup];
+    const int vc = min(v, nvec - 1);
 #pragma unroll
     for (int g = 0; g < kGroup; ++g)
-      yv[g] = active && row[g] >= 0 ? load_stream(&y[(size_t)row[g] * nvec + v])
-                                    : make_uint4(0, 0, 0, 0);
+      yv[g] = j0 + g < k ? load_stream(&y[(size_t)max(row[g], 0) * nvec + vc])
+                         : make_uint4(0, 0, 0, 0);
     fold_rows<kGroup>(acc, yv, row, wj);
+    // every gathered value is consumed on every path, so no load is moved
+    // into the fold's per-row branches
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g)
+      if (j0 + g < k) asm volatile("" ::"v"(yv[g].x));
   }
   if (!active) return;
   uint4 o;
