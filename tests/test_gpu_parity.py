@@ -281,6 +281,7 @@ def test_fp8_quantiser_at_extreme_magnitudes(T, k, payload_path):
     (100, 512, 8, 3, 8, 0.0, False),   # 8 lanes per group, 8 logits per lane
     (50, 256, 1, 1, 8, 0.0, False),    # one group: plain top-k
     (90, 320, 8, 3, 8, 0.0, True),     # 5 experts per lane, 8 lanes per group
+    (90, 320, 8, 3, 8, 1.2, False),    # the same with a popularity bias
     (70, 96, 3, 2, 6, 0.0, False),     # 3 groups of 16 lanes, lanes 48-63 empty
     (30, 1024, 16, 6, 8, 0.0, True),   # 16 experts per lane, 4 lanes per group
     (40, 8, 4, 2, 2, 0.0, True),       # 2 lanes per group, 56 empty lanes
