@@ -87,6 +87,8 @@ SWEEP = [
     (64, 32768, 64, 4, 8, 0, 0, True, None),       # wide rows: 8 column chunks per token
     (40, 16384, 32, 8, 4, 320, 1, True, None),     # wide fp8 rows, 128 scale blocks
     (700, 20480, 64, 8, 8, 0, 0, False, 1),        # wide rows on the chunked path
+    (600, 2048, 1024, 8, 64, 0, 1, True, None),    # fp8, E at the library maximum, chunked
+    (100, 1024, 512, 32, 16, 3200, 1, False, 3),   # fp8, k at the library maximum, repeats
 ]
 
 
