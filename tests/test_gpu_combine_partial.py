@@ -28,6 +28,9 @@ pytestmark = pytest.mark.gpu
     (50, 536, 64, 8, 8, 0, 0, False),          # ragged row: last chunk has 3 live lanes < k
     (0, 256, 16, 4, 4, 0, 0, False),           # no tokens
     (2400, 7168, 256, 8, 32, 0, 0, False),     # 34 MB output: device-scope stores
+    (60, 512, 1024, 32, 32, 0, 0, False),      # k and E at the library maximum
+    (40, 1024, 1024, 32, 64, 0, 1, False),     # the same with fp8, 64 ranks
+    (80, 256, 16, 4, 1, 0, 0, False),          # one rank: one partial row per token
 ])
 def test_two_stage_combine(T, H, E, k, N, C, payload, skew):
     print(f"[case] two-stage T={T} H={H} E={E} k={k} N={N} C={C} p={payload}", flush=True)
