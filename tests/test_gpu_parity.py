@@ -319,6 +319,7 @@ def test_grouped_route(T, E, G, TG, k, zipf, ties):
     (6, 256, 512, 64, 8, 8, 1500, 1),
     (4, 128, 256, 32, 8, 4, 0, 0),
     (5, 256, 256, 48, 4, 6, 900, 0),
+    (2, 100, 256, 1024, 32, 32, 0, 0),    # E and k at the library maximum, chunked
 ])
 def test_dispatch_sources(S, T, H, E, k, N, C, payload):
     """Every source rank dispatching at once: segments in (source, token, slot)

@@ -45,6 +45,7 @@ def _host(t, fp8):
     (1040, 256, 64, 8, 8, 1000, 1, 2),        # > 8192 rows: 4 rows per wave, fp8, overflow
     (100, 512, 30, 4, 5, 100, 0, None),       # E not a multiple of 4: 4-byte count loads
     (60, 1024, 90, 6, 6, 0, 1, 2),            # the same, fp8, packed regions
+    (40, 512, 256, 32, 32, 0, 0, None),       # k at the library maximum
 ])
 def test_split_chain(T, H, E, k, N, C, payload, hot):
     print(f"[case] split T={T} H={H} E={E} k={k} N={N} C={C} p={payload}", flush=True)
