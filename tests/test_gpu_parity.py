@@ -175,9 +175,12 @@ def test_route_signed_zero_logits():
         assert np.array_equal(ids.cpu().numpy(), o_ids)
 
 
-def test_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("grouped", [False, True])
+def test_graph_capture_replays_match_eager(grouped):
     """route -> dispatch -> combine captured once and replayed several times,
-    with eager work between replays; every replay equals the eager result."""
+    with eager work between replays; every replay equals the eager result.
+    grouped: the group-limited router (4 of 8 groups) in place of plain top-k."""
+    _announce(f"graph capture, grouped router {grouped}")
     w = inputs.WORKLOADS["dsv3_decode"]
     inp = inputs.generate_for(w)
     shape = workload_shape(w)
@@ -190,7 +193,10 @@ def test_graph_capture_replays_match_eager():
     out = torch.empty(w.T, w.H, dtype=torch.int16, device="cuda")
 
     def step(stream=None):
-        api.moe_route_topk(lg, None, w.k, w.score, ids, wt, stream=stream)
+        if grouped:
+            api.moe_route_topk_grouped(lg, None, w.k, w.score, 8, 4, ids, wt, stream=stream)
+        else:
+            api.moe_route_topk(lg, None, w.k, w.score, ids, wt, stream=stream)
         api.moe_dispatch(shape, x, ids, recv, None, lay, None, stream=stream)
         api.moe_combine(shape, recv, None, lay, wt, out, stream=stream)
 
@@ -209,6 +215,7 @@ def test_graph_capture_replays_match_eager():
     for i in range(4):
         out.fill_(0)
         lay.token_row.fill_(-7)
+        ids.fill_(-1)
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {i}"
