@@ -295,7 +295,8 @@ def test_fp8_quantiser_at_extreme_magnitudes(T, k, payload_path):
     (30, 1024, 16, 6, 8, 0.0, True),   # 16 experts per lane, 4 lanes per group
     (40, 8, 4, 2, 2, 0.0, True),       # 2 lanes per group, 56 empty lanes
     (60, 40, 5, 2, 4, 0.0, False),     # 5 groups of 8 lanes
-    # groups that do not fall on whole lanes: LDS copy, one lane per group
+    # groups off whole lanes, or wider than the 16-lane DPP merge: LDS copy,
+    # one lane per group
     (100, 160, 8, 3, 8, 0.0, True),    # 20 experts per group, 3 per lane
     (80, 120, 8, 3, 6, 0.0, False),    # 15 experts per group (scalar LDS reads)
     (60, 256, 2, 1, 8, 0.0, True),     # 32 lanes per group
