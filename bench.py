@@ -8,16 +8,21 @@ runs once per buffer set before timing, so combine reads expert outputs that
 are really in HBM.  Inputs are seeded synthetic data of the workload's shape,
 resident in HBM before the timed region.
 
-Cold (headline): S buffer sets rotate so that the bytes touched between two
-uses of a set exceed twice the 256 MB Infinity Cache.  Warm: one set, reused
+Cold (headline): each timed graph rotates through S buffer sets, S sized from
+that graph's own bytes so that the bytes it touches between two uses of a set
+exceed twice the 256 MB Infinity Cache.  Warm: one set, reused
 (cache-assisted), reported alongside.  Stream floor: plain streaming read and
 write kernels (libmoe_ceiling.so) over the payload size, timed the same way,
 give what the memory system sustains at that size.
 
 Timing: HIP graphs of back-to-back launches replayed between HIP events on the
-launch stream.  The step figure captures K whole steps (one timed replay);
-each kernel's average launch duration comes from a graph of K launches of that
-kernel alone (median of three timed replays).
+launch stream.  A kernel's per-launch time is the difference of a graph of 2n
+launches and one of n launches, divided by n (n = the smallest multiple of the
+graph's S that is at least K), so the fixed cost of a replay cancels and the
+buffer rotation continues unbroken from one replay to the next; the median and
+the 10th and 90th percentiles over --reps replay pairs are reported.
+ms_per_step is one replay of exactly K whole steps (route, dispatch, combine),
+synchronised on both sides.
 
 Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -65,6 +70,19 @@ def parse():
     ap.add_argument("--no-next", action="store_true",
                     help="skip the timings of the adjacent paths (partial-reduction combine, "
                          "receive-side shuffle, group-limited router) in the default run")
+    ap.add_argument("--reps", type=int, default=7,
+                    help="timed replay pairs per graph (median and percentiles over them)")
+    ap.add_argument("--summarize-profile", action="store_true",
+                    help="print the summary of rocprofv3 output (--trace-dir, and optionally "
+                         "--fetch-dir/--write-dir/--cal-fetch-dir/--cal-write-dir) for these "
+                         "options instead of running")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--cal-fetch-dir")
+    ap.add_argument("--cal-write-dir")
+    ap.add_argument("--write-figures", action="store_true",
+                    help="with --summarize-profile: also write profiles/figures_<options>.txt")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (PMC scale factor)")
     return ap.parse_args()
@@ -123,10 +141,11 @@ def profile_tag(args):
     return tag
 
 
-def read_traffic(tag, kernel):
-    """HBM bytes per launch from a committed PMC summary, if it was taken on
-    the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.txt")
+def read_figure(tag, part, key):
+    """A figure of one step part from the committed profile summary of these
+    options (PMC traffic per launch, rocprofv3 kernel durations), if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"figures_{tag}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -134,10 +153,10 @@ def read_traffic(tag, kernel):
         if "=" in line and not line.startswith("#"):
             a, b = line.split("=", 1)
             kv[a.strip()] = b.strip()
-    if kv.get(f"{kernel}_source_sha") != source_sha(kernel):
+    if kv.get(f"{part}_source_sha") != source_sha(part):
         return None
-    val = kv.get(f"{kernel}_traffic_bytes_per_launch")
-    return None if val is None else float(val)
+    val = kv.get(f"{part}_{key}")
+    return None if val in (None, "", "None") else float(val)
 
 
 # ---------------------------------------------------------------------------
@@ -185,6 +204,79 @@ class BufferSet:
             self.ey, self.eys = api.alloc_recv(shape, dev)
 
 
+def sets_for(nbytes, cap):
+    """Buffer sets a timed graph rotates through so that the bytes it touches
+    between two uses of one set exceed twice the Infinity Cache (at least 2,
+    at most `cap`)."""
+    return max(2, min(cap, math.ceil(2 * MALL_BYTES / max(nbytes, 1))))
+
+
+class GraphTimer:
+    """Per-launch time of one launch kind, measured as the difference of two
+    HIP graphs of n and 2n back-to-back launches (n a whole multiple of the
+    graph's S buffer sets, launch i using set i mod S), each replayed between
+    HIP events on the launch stream: (t(2n) - t(n)) / n.  The fixed cost of a
+    replay cancels, so the figure does not depend on --steps, and because each
+    replay ends on set S-1 and the next starts on set 0, the rotation runs on
+    unbroken across replays.  `reps` pairs of replays give the median and the
+    10th and 90th percentiles of the estimate."""
+
+    def __init__(self, torch, stream, reps):
+        self.torch, self.stream, self.reps = torch, stream, reps
+
+    def capture(self, launch, n):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            for i in range(n):
+                launch(i)
+        return g
+
+    def replay_us(self, g):
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        # replay() launches on torch's current stream: make that the launch
+        # stream and record the events on it
+        with torch.cuda.stream(self.stream):
+            e0.record(self.stream)
+            g.replay()
+            e1.record(self.stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    def per_launch(self, launch, S, K):
+        n1 = S * -(-K // S)
+        g1, g2 = self.capture(launch, n1), self.capture(launch, 2 * n1)
+        self.replay_us(g1)   # warm-up replays (code, page tables)
+        self.replay_us(g2)
+        d = []
+        for _ in range(self.reps):
+            t1 = self.replay_us(g1)
+            t2 = self.replay_us(g2)
+            d.append((t2 - t1) / n1)
+        del g1, g2
+        return summarize(d, n1, S)
+
+    def one_replay_us(self, launch, n):
+        """Time of one replay of a graph of exactly n launches (after one
+        untimed replay), synchronized on both sides."""
+        g = self.capture(launch, n)
+        self.replay_us(g)
+        self.torch.cuda.synchronize()
+        t = self.replay_us(g)
+        self.torch.cuda.synchronize()
+        del g
+        return t
+
+
+def summarize(d, n, S):
+    import numpy as np
+    a = np.asarray(d, dtype=np.float64)
+    return {"us": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "launches": [n, 2 * n], "sets": S}
+
+
 def run_gpu(args, w, inp):
     import numpy as np
     import torch
@@ -197,8 +289,14 @@ def run_gpu(args, w, inp):
                     else api.MOE_PAYLOAD_BF16)
     shape = api.world_shape(one, w.sources)  # all sources' tokens together
     nbytes = algorithmic_bytes(w)
-    per_step = nbytes["dispatch"] + nbytes["combine"] + nbytes["route"]
-    S = args.sets or min(64, max(2, math.ceil(2 * MALL_BYTES / per_step)))
+    cap = args.sets or 64
+    # each timed graph rotates through as many sets as its own bytes need
+    s_disp = sets_for(nbytes["dispatch"], cap)
+    s_comb = sets_for(nbytes["combine"], cap)
+    s_route = sets_for(nbytes["route"], cap)
+    s_step = sets_for(nbytes["dispatch"] + nbytes["combine"] + nbytes["route"], cap)
+    S = max(s_disp, s_comb)
+    s_route = min(s_route, S)
     # adjacent paths timed beside the main one (cold only), on the same sets
     nxt = not args.no_next
     grouping = next_grouping(w) if nxt and args.groups <= 1 else None
@@ -226,7 +324,7 @@ def run_gpu(args, w, inp):
 
     def combine_send(s):
         api.moe_combine_partial_send(shape, s.y, s.ys, s.lay, s.ids, s.w, s.partial, s.prank,
-                             stream=stream)
+                                     stream=stream)
 
     def combine_recv(s):
         api.moe_combine_partial_recv(shape, s.partial, s.prank, s.out, stream=stream)
@@ -261,90 +359,49 @@ def run_gpu(args, w, inp):
             combine(s)
             if two_stage_t and not two_stage:
                 combine_send(s)
+            if split_t:
+                dispatch_recv(s)
     stream.synchronize()
     status = int(sets[0].lay.status.item())
     partial_rows = int((sets[0].prank >= 0).sum().item()) if two_stage_t else 0
     placed_rows = int((sets[0].lay.token_row >= 0).sum().item())
 
-    def capture(fn_list, n, rotate):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(n):
-                s = sets[i % len(sets)] if rotate else sets[0]
-                for fn in fn_list:
-                    fn(s)
-        return g
-
-    def time_graph(g, n, reps=1):
-        # replay() launches on torch's current stream: make that the launch
-        # stream, and bracket the replay with events recorded on it.  With
-        # reps > 1 the median of that many timed replays is returned.
-        ts = []
-        for _ in range(reps):
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            with torch.cuda.stream(stream):
-                e0.record(stream)
-                g.replay()
-                e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3 / n)  # us per unit
-        return sorted(ts)[len(ts) // 2]
-
+    timer = GraphTimer(torch, stream, args.reps)
     K, W = args.steps, args.warmup
-    res = {"sets": S, "status": status, "partial_rows": partial_rows, "placed_rows": placed_rows}
-    for mode, rotate in (("cold", True), ("warm", False)):
+
+    def on(fn, n_sets):
+        return lambda i: fn(sets[i % n_sets])
+
+    res = {"sets": {"dispatch": s_disp, "combine": s_comb, "route": s_route, "step": s_step},
+           "status": status, "partial_rows": partial_rows, "placed_rows": placed_rows}
+    for mode in ("cold", "warm"):
         if mode == "warm" and args.no_warm:
             continue
-        # warm-up: W eager steps, then one replay of each graph
+        cold = mode == "cold"
+        sd, sc, sr, ss = (s_disp, s_comb, s_route, s_step) if cold else (1, 1, 1, 1)
+        # W untimed eager steps, then the K-step graph of the contract
         with torch.cuda.stream(stream):
             for i in range(W):
-                step(sets[i % len(sets)] if rotate else sets[0])
+                step(sets[i % ss])
         stream.synchronize()
-        g_step = capture([route, dispatch, combine], K, rotate)
-        g_route = capture([route], K, rotate)
-        g_disp = capture([dispatch], K, rotate)
-        g_comb = capture([combine], K, rotate)
-        with torch.cuda.stream(stream):
-            for g in (g_step, g_route, g_disp, g_comb):
-                g.replay()
-        torch.cuda.synchronize()
-        step_us = time_graph(g_step, K)
-        r = {
-            "step_us": step_us,
-            "route_us": time_graph(g_route, K, reps=3),
-            "dispatch_us": time_graph(g_disp, K, reps=3),
-            "combine_us": time_graph(g_comb, K, reps=3),
-        }
-        if two_stage or (two_stage_t and mode == "cold"):
-            g_send = capture([combine_send], K, rotate)
-            g_recv = capture([combine_recv], K, rotate)
-            with torch.cuda.stream(stream):
-                g_send.replay()
-                g_recv.replay()
-            r["combine_send_us"] = time_graph(g_send, K, reps=3)
-            r["combine_recv_us"] = time_graph(g_recv, K, reps=3)
-            del g_send, g_recv
-        if args.split or (split_t and mode == "cold"):
-            g_dr = capture([dispatch_recv], K, rotate)
-            g_cs = capture([combine_send_back], K, rotate)
-            with torch.cuda.stream(stream):
-                g_dr.replay()
-                g_cs.replay()
-            r["dispatch_recv_us"] = time_graph(g_dr, K, reps=3)
-            r["combine_send_back_us"] = time_graph(g_cs, K, reps=3)
-            del g_dr, g_cs
-        if grouping is not None and mode == "cold":
-            g_rg = capture([route_grouped], K, rotate)
-            with torch.cuda.stream(stream):
-                g_rg.replay()
-            r["route_grouped_us"] = time_graph(g_rg, K, reps=3)
-            del g_rg
+        r = {"step_replay_us": timer.one_replay_us(on(step, ss), K),
+             "step": timer.per_launch(on(step, ss), ss, K),
+             "route": timer.per_launch(on(route, sr), sr, K),
+             "dispatch": timer.per_launch(on(dispatch, sd), sd, K),
+             "combine": timer.per_launch(on(combine, sc), sc, K)}
+        if cold and (two_stage or two_stage_t):
+            r["combine_send"] = timer.per_launch(on(combine_send, sc), sc, K)
+            r["combine_recv"] = timer.per_launch(on(combine_recv, sc), sc, K)
+        if cold and split_t:
+            r["dispatch_recv"] = timer.per_launch(on(dispatch_recv, sd), sd, K)
+            r["combine_send_back"] = timer.per_launch(on(combine_send_back, sc), sc, K)
+        if cold and grouping is not None:
+            r["route_grouped"] = timer.per_launch(on(route_grouped, sr), sr, K)
         res[mode] = r
-        del g_step, g_route, g_disp, g_comb
+    del sets
+    torch.cuda.empty_cache()
     if not args.no_floor:
-        res["floor"] = stream_floor(torch, stream, time_graph, payload_bytes(w), min(K, 100))
+        res["floor"] = stream_floor(torch, stream, timer, payload_bytes(w), K)
     return res
 
 
@@ -373,10 +430,10 @@ def payload_bytes(w):
     return w.tokens * w.k * nbytes_row(w)
 
 
-def stream_floor(torch, stream, time_graph, nbytes, n):
+def stream_floor(torch, stream, timer, nbytes, K):
     """What the memory system sustains at this size: plain streaming read and
     write of `nbytes` with 16-byte accesses, and an empty launch, timed like
-    the kernels (graphs of n launches over rotating buffers, cold).  Read: a
+    the kernels (graph differences over rotating buffers, cold).  Read: a
     non-temporal grid-stride loop, the best of three grid sizes.  Write: the
     best of that loop and of 64 KB blocks stored with each cache policy.
     Copy: read and write of `nbytes` each, the non-temporal loop."""
@@ -389,7 +446,7 @@ def stream_floor(torch, stream, time_graph, nbytes, n):
     lib.moe_ceiling_copy.argtypes = [vp, vp, sz, i32, vp]
     lib.moe_ceiling_empty.argtypes = [vp]
     nbytes = (nbytes + 15) // 16 * 16
-    S = min(64, max(2, math.ceil(2 * MALL_BYTES / nbytes)))
+    S = sets_for(nbytes, 64)
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(S)]
     for b in bufs:
         b.fill_(1)
@@ -398,16 +455,9 @@ def stream_floor(torch, stream, time_graph, nbytes, n):
     st = stream.cuda_stream
 
     def timed(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(n):
-                assert fn(i) == 0
-        with torch.cuda.stream(stream):
-            g.replay()
-        torch.cuda.synchronize()
-        t = time_graph(g, n, reps=3)
-        del g
-        return t
+        def launch(i):
+            assert fn(i) == 0
+        return timer.per_launch(launch, S, K)["us"]
 
     grids = (1024, 2048, 4096)
     rd = min(timed(lambda i, b=b: lib.moe_ceiling_read(bufs[i % S].data_ptr(), nvec,
@@ -425,7 +475,8 @@ def stream_floor(torch, stream, time_graph, nbytes, n):
     em = timed(lambda i: lib.moe_ceiling_empty(st))
     del bufs
     torch.cuda.empty_cache()
-    return {"bytes": nbytes, "read_us": rd, "write_us": wr, "copy_us": cp, "empty_launch_us": em}
+    return {"bytes": nbytes, "sets": S, "read_us": rd, "write_us": wr, "copy_us": cp,
+            "empty_launch_us": em}
 
 
 def cpu_baseline(w, inp, seconds):
@@ -492,6 +543,140 @@ def cpu_model():
     return platform.processor() or platform.machine()
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (what profiles/ holds)
+# ---------------------------------------------------------------------------
+# kernels that make up each step part (name fragments as rocprofv3 prints them)
+PART_KERNELS = {
+    "route": ["route_topk_kernel"],
+    "dispatch": ["dispatch_fused_kernel", "layout_chunk_kernel", "layout_scan_kernel",
+                 "dispatch_scatter_kernel", "source_counts_kernel", "source_offsets_kernel",
+                 "source_from_bases_kernel"],
+    "combine": ["combine_bf16_kernel", "combine_fp8_kernel", "combine_send_kernel",
+                "combine_send_small_kernel", "combine_recv_kernel"],
+}
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _part_of(name):
+    for part, frags in PART_KERNELS.items():
+        for f in frags:
+            if f in name:
+                return part, f
+    return None, None
+
+
+def summarize_profile(args):
+    """Markdown summary of a rocprofv3 kernel trace (and optional FETCH_SIZE /
+    WRITE_SIZE counter runs with their copy calibration) for this workload and
+    options; with --write-figures also the key = value file bench.py reads."""
+    import numpy as np
+    from combine_moe_dispatch_amd import inputs
+    w = inputs.WORKLOADS[args.workload]
+    nb = algorithmic_bytes(w)
+    tag = profile_tag(args)
+    out = []
+    figures = {}
+    # kernel trace: per kernel, every dispatch's end - start
+    rows = _csv_rows(args.trace_dir, "kernel_trace.csv")
+    durs = {}
+    for r in rows:
+        durs.setdefault(r["Kernel_Name"], []).append(
+            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out.append("| kernel | calls | mean ns | median ns | p10 ns | p90 ns | min ns | max ns |")
+    out.append("|---|---|---|---|---|---|---|---|")
+    per_frag = {}
+    for name, d in sorted(durs.items(), key=lambda kv: -len(kv[1])):
+        a = np.asarray(d, np.float64)
+        short = name.replace("void ", "").replace("(anonymous namespace)::", "")
+        short = short.replace("moe::", "").split("(")[0]
+        out.append(f"| {short[:60]} | {len(a)} | {a.mean():.0f} | {np.median(a):.0f} | "
+                   f"{np.percentile(a, 10):.0f} | {np.percentile(a, 90):.0f} | {a.min():.0f} | "
+                   f"{a.max():.0f} |")
+        part, frag = _part_of(name)
+        if part:
+            per_frag.setdefault((part, frag), []).extend(d)
+    out.append("")
+    out.append("| step part | kernels | rocprofv3 median us (sum over the part's kernels) | "
+               "mean us | algorithmic bytes | GB/s at the median | fraction of 8 TB/s |")
+    out.append("|---|---|---|---|---|---|---|")
+    for part in ("route", "dispatch", "combine"):
+        ks = [(f, d) for (p, f), d in per_frag.items() if p == part]
+        if not ks:
+            continue
+        med = sum(float(np.median(d)) for _, d in ks) / 1e3
+        mean = sum(float(np.mean(d)) for _, d in ks) / 1e3
+        gbs = nb[part] / (med * 1e-6) / 1e9
+        figures[f"{part}_rocprof_median_us"] = f"{med:.3f}"
+        figures[f"{part}_rocprof_mean_us"] = f"{mean:.3f}"
+        out.append(f"| {part} | {', '.join(f for f, _ in ks)} | {med:.3f} | {mean:.3f} | "
+                   f"{nb[part]} | {gbs:.0f} | {gbs / HBM_PEAK_GBS:.4f} |")
+    # counters, scaled by what the same counter reads for a copy of known size
+    if args.fetch_dir and args.write_dir and args.cal_fetch_dir and args.cal_write_dir:
+        def per_kernel(directory, counter):
+            acc = {}
+            for r in _csv_rows(directory, "counter_collection.csv"):
+                if r["Counter_Name"] != counter:
+                    continue
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            return acc
+
+        def copy_kib(directory, counter):
+            vals = [v for name, v in per_kernel(directory, counter).items()
+                    if "copy" in name.lower() or "elementwise" in name.lower()]
+            best = max(vals, key=len)  # the copy launches (the most numerous)
+            return float(np.median(best))
+        gib_kib = float(1 << 20)  # 1 GiB in KiB
+        fscale = gib_kib / copy_kib(args.cal_fetch_dir, "FETCH_SIZE")
+        wscale = gib_kib / copy_kib(args.cal_write_dir, "WRITE_SIZE")
+        fk = per_kernel(args.fetch_dir, "FETCH_SIZE")
+        wk = per_kernel(args.write_dir, "WRITE_SIZE")
+        out.append("")
+        out.append(f"Copy calibration (a 1 GiB device copy): FETCH_SIZE x {fscale:.4f}, "
+                   f"WRITE_SIZE x {wscale:.4f}.")
+        out.append("")
+        out.append("| kernel | FETCH_SIZE KiB per dispatch | WRITE_SIZE KiB per dispatch | "
+                   "scaled bytes |")
+        out.append("|---|---|---|---|")
+        part_bytes = {}
+        for name in sorted(set(fk) | set(wk)):
+            part, frag = _part_of(name)
+            if not part:
+                continue
+            f = float(np.median(fk.get(name, [0.0])))
+            wv = float(np.median(wk.get(name, [0.0])))
+            b = 1024.0 * (f * fscale + wv * wscale)
+            part_bytes[part] = part_bytes.get(part, 0.0) + b
+            out.append(f"| {frag} | {f:.1f} | {wv:.1f} | {b:.0f} |")
+        out.append("")
+        out.append("| step part | scaled bytes per launch | algorithmic bytes | ratio |")
+        out.append("|---|---|---|---|")
+        for part, b in part_bytes.items():
+            figures[f"{part}_traffic_bytes_per_launch"] = f"{b:.0f}"
+            out.append(f"| {part} | {b:.0f} | {nb[part]} | {b / nb[part]:.3f} |")
+        figures["fetch_scale"] = f"{fscale:.6f}"
+        figures["write_scale"] = f"{wscale:.6f}"
+    print("\n".join(out))
+    if args.write_figures:
+        path = os.path.join(ROOT, "profiles", f"figures_{tag}.txt")
+        with open(path, "w") as f:
+            f.write(f"# {tag}: figures from rocprofv3 (bench.py --summarize-profile); each part's\n"
+                    f"# figures hold for the kernel sources with its hash\n")
+            for part in ("route", "dispatch", "combine"):
+                f.write(f"{part}_source_sha = {source_sha(part)}\n")
+            for k, v in sorted(figures.items()):
+                f.write(f"{k} = {v}\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -501,6 +686,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.summarize_profile:
+        summarize_profile(args)
         return
 
     from combine_moe_dispatch_amd import inputs
@@ -516,12 +704,13 @@ def main():
         nbytes["combine"] = send + recv
         nbytes["combine_send"], nbytes["combine_recv"] = send, recv
     cold = g["cold"]
-    dc_us = cold["dispatch_us"] + cold["combine_us"]
+    us = {k: v["us"] for k, v in cold.items() if isinstance(v, dict)}
+    dc_us = us["dispatch"] + us["combine"]
     dc_bytes = nbytes["dispatch"] + nbytes["combine"]
     value = dc_bytes / (dc_us * 1e-6) / 1e9
-    dom = "dispatch" if cold["dispatch_us"] >= cold["combine_us"] else "combine"
-    dom_us = cold[f"{dom}_us"]
-    achieved = nbytes[dom] / (dom_us * 1e-6) / 1e9
+    dom = "dispatch" if us["dispatch"] >= us["combine"] else "combine"
+    achieved = nbytes[dom] / (us[dom] * 1e-6) / 1e9
+    tag = profile_tag(args)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -529,7 +718,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(cold["step_us"] / 1e3, 6),
+        "ms_per_step": round(cold["step_replay_us"] / args.steps / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -544,65 +733,84 @@ def main():
                    "router": ("top-k" if args.groups <= 1 else
                               f"group-limited top-k, {args.topk_groups} of {args.groups} groups"),
                    "cold_buffer_sets": g["sets"]},
-        "dispatch_us": round(cold["dispatch_us"], 3),
-        "combine_us": round(cold["combine_us"], 3),
+        "dispatch_us": round(us["dispatch"], 3),
+        "combine_us": round(us["combine"], 3),
         "dispatch_plus_combine_us": round(dc_us, 3),
-        "route_us": round(cold["route_us"], 3),
-        "step_us": round(cold["step_us"], 3),
+        "route_us": round(us["route"], 3),
+        "step_us": round(us["step"], 3),
         "hbm_frac_dispatch_plus_combine": round(value / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": nbytes,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": read_traffic(profile_tag(args), dom)},
+                     "traffic": read_figure(tag, dom, "traffic_bytes_per_launch")},
+        "timing": {
+            "method": "per launch = (t(2n) - t(n)) / n for HIP graphs of n and 2n back-to-back "
+                      "launches, n a multiple of the graph's buffer sets; median and "
+                      "10th/90th percentiles over replay pairs",
+            "replay_pairs": args.reps,
+            **{k: {"us": round(v["us"], 3), "p10": round(v["p10"], 3),
+                   "p90": round(v["p90"], 3), "launches": v["launches"], "sets": v["sets"]}
+               for k, v in cold.items() if isinstance(v, dict)}},
         "device_status": g["status"],
     }
+    prof = {}
+    for part in ("route", "dispatch", "combine"):
+        med = read_figure(tag, part, "rocprof_median_us")
+        mean = read_figure(tag, part, "rocprof_mean_us")
+        if med is not None:
+            prof[part] = {"median_us": med, "mean_us": mean,
+                          "median_over_event": round(med / us[part], 3)}
+    if prof:
+        # kernel durations of the committed rocprofv3 trace of these sources
+        line["rocprof_kernel_trace"] = prof
     send_b, recv_b = two_stage_bytes(w, g["partial_rows"])
     # receive-side shuffle: each placed row read once and written once, plus
     # (counts, offsets) per expert read and the dense offsets written
     moved = 2 * g["placed_rows"] * nbytes_row(w) + 8 * w.E + 4 * (w.E + 1)
     extra = {}
-    if "combine_send_us" in cold:
+    if "combine_send" in us:
         extra["combine_partial"] = {
-            "send_us": round(cold["combine_send_us"], 3), "recv_us": round(cold["combine_recv_us"], 3),
+            "send_us": round(us["combine_send"], 3), "recv_us": round(us["combine_recv"], 3),
             "partial_rows": g["partial_rows"], "rows_per_token": round(g["partial_rows"] / w.tokens, 3),
-            "send_GBps": round(send_b / (cold["combine_send_us"] * 1e-6) / 1e9, 1),
-            "recv_GBps": round(recv_b / (cold["combine_recv_us"] * 1e-6) / 1e9, 1)}
-    if "dispatch_recv_us" in cold:
+            "send_GBps": round(send_b / (us["combine_send"] * 1e-6) / 1e9, 1),
+            "recv_GBps": round(recv_b / (us["combine_recv"] * 1e-6) / 1e9, 1)}
+    if "dispatch_recv" in us:
         extra["split"] = {
-            "dispatch_recv_us": round(cold["dispatch_recv_us"], 3),
-            "combine_send_us": round(cold["combine_send_back_us"], 3),
+            "dispatch_recv_us": round(us["dispatch_recv"], 3),
+            "combine_send_us": round(us["combine_send_back"], 3),
             "bytes_each": moved,
-            "dispatch_recv_GBps": round(moved / (cold["dispatch_recv_us"] * 1e-6) / 1e9, 1),
-            "combine_send_GBps": round(moved / (cold["combine_send_back_us"] * 1e-6) / 1e9, 1)}
-    if "route_grouped_us" in cold:
+            "dispatch_recv_GBps": round(moved / (us["dispatch_recv"] * 1e-6) / 1e9, 1),
+            "combine_send_GBps": round(moved / (us["combine_send_back"] * 1e-6) / 1e9, 1)}
+    if "route_grouped" in us:
         G, kept = next_grouping(w)
         extra["route_grouped"] = {"groups": G, "groups_kept": kept,
-                                  "route_us": round(cold["route_grouped_us"], 3)}
+                                  "route_us": round(us["route_grouped"], 3)}
     if args.combine == "two-stage":
         line["two_stage_combine"] = extra.pop("combine_partial")
     if args.split:
         line["split"] = extra.pop("split")
     if extra:
-        # adjacent paths on the same inputs, cold, one graph of K launches each
+        # adjacent paths on the same inputs, cold, timed like the main kernels
         line["next"] = extra
     if "warm" in g:
-        wm = g["warm"]
-        wus = wm["dispatch_us"] + wm["combine_us"]
+        wm = {k: v["us"] for k, v in g["warm"].items() if isinstance(v, dict)}
+        wus = wm["dispatch"] + wm["combine"]
         line["warm_cache_assisted"] = {
-            "dispatch_us": round(wm["dispatch_us"], 3), "combine_us": round(wm["combine_us"], 3),
-            "route_us": round(wm["route_us"], 3), "step_us": round(wm["step_us"], 3),
+            "dispatch_us": round(wm["dispatch"], 3), "combine_us": round(wm["combine"], 3),
+            "route_us": round(wm["route"], 3), "step_us": round(wm["step"], 3),
             "GBps": round(dc_bytes / (wus * 1e-6) / 1e9, 2)}
     if "floor" in g:
         fl = g["floor"]
         line["stream_floor"] = {
-            "payload_bytes": fl["bytes"], "read_us": round(fl["read_us"], 3),
+            "payload_bytes": fl["bytes"], "sets": fl["sets"], "read_us": round(fl["read_us"], 3),
             "write_us": round(fl["write_us"], 3), "copy_us": round(fl["copy_us"], 3),
             "empty_launch_us": round(fl["empty_launch_us"], 3),
             "read_GBps": round(fl["bytes"] / (fl["read_us"] * 1e-6) / 1e9, 1),
             "write_GBps": round(fl["bytes"] / (fl["write_us"] * 1e-6) / 1e9, 1),
-            "dispatch_over_write_floor": round(cold["dispatch_us"] / fl["write_us"], 3),
-            "combine_over_read_floor": round(cold["combine_us"] / fl["read_us"], 3)}
+            "write_plus_read_us": round(fl["write_us"] + fl["read_us"], 3),
+            "dispatch_over_write_floor": round(us["dispatch"] / fl["write_us"], 3),
+            "combine_over_read_floor": round(us["combine"] / fl["read_us"], 3)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

@@ -38,6 +38,26 @@ def test_algorithmic_bytes_are_payload_plus_metadata(name):
     assert bench.payload_bytes(w) == payload
 
 
+def test_cold_sets_exceed_twice_the_cache_per_graph():
+    """Each timed graph rotates through enough sets that the bytes it touches
+    between two uses of a set exceed twice the 256 MB Infinity Cache."""
+    w = inputs.WORKLOADS["dsv3_decode"]
+    nb = bench.algorithmic_bytes(w)
+    for part in ("dispatch", "combine"):
+        S = bench.sets_for(nb[part], 64)
+        assert S * nb[part] >= 2 * bench.MALL_BYTES
+        assert (S - 1) * nb[part] < 2 * bench.MALL_BYTES  # no more than needed
+    assert bench.sets_for(nb["dispatch"], 64) == 33
+    # a launch that alone exceeds the cache still alternates two sets
+    assert bench.sets_for(1 << 30, 64) == 2
+
+
+def test_per_launch_statistics():
+    st = bench.summarize([4.0, 5.0, 4.5, 4.4, 4.6], 33, 33)
+    assert st["us"] == 4.5 and st["launches"] == [33, 66] and st["sets"] == 33
+    assert 4.0 <= st["p10"] <= st["us"] <= st["p90"] <= 5.0
+
+
 def test_decode_payload_matches_the_worked_size():
     # DeepSeek-V3 decode: 128 tokens x 8 rows x 7168 bf16 values = 14,680,064 bytes
     # each way; with the token rows (1,835,008 bytes) 16,515,072
@@ -69,6 +89,12 @@ def test_bench_prints_one_contract_line():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
     assert d["device_status"] == 0
+    tm = d["timing"]
+    for part in ("route", "dispatch", "combine", "step"):
+        assert tm[part]["p10"] <= tm[part]["us"] <= tm[part]["p90"], part
+        n1, n2 = tm[part]["launches"]
+        assert n2 == 2 * n1 and n1 % tm[part]["sets"] == 0 and n1 >= 5
+    assert d["dispatch_us"] == tm["dispatch"]["us"]
     # the adjacent paths timed in the default run
     nx = d["next"]
     assert set(nx) == {"combine_partial", "split", "route_grouped"}

@@ -1,0 +1,105 @@
+"""GPU parity of the router at the library's advertised limits.
+
+The header allows k up to 32 and E up to 1024.  These cases run the plain
+router on every per-lane width the kernel is built for (1, 2, 4, 6, 8 and 16
+logits per lane: E in 1..64, 65..128, 129..256, 257..384, 385..512 and
+513..1024), with k past 8 (the top-k rounds beyond one DPP row of slots) and
+past 16 (the weight sum over the second row of slot lanes), and the
+group-limited router with k past 8.  Inputs: N(0,1) logits with an N(0,1)
+bias, and integer logits with a half-integer bias (many exact ties, which the
+selection breaks toward the lower expert id).  Bars as elsewhere: ids
+bit-exact, weights within 2^-20 relative of the oracle's double-precision
+weights rounded once to fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_moe_dispatch_amd import api
+
+pytestmark = pytest.mark.gpu
+
+WEIGHT_RTOL = 2.0 ** -20
+
+
+def _logits(T, E, ties, seed):
+    rng = np.random.default_rng(seed)
+    if ties:
+        lg = rng.integers(-3, 4, size=(T, E)).astype(np.float32)
+        bias = (rng.integers(-2, 3, size=E) * 0.5).astype(np.float32)
+    else:
+        lg = rng.standard_normal((T, E), dtype=np.float32)
+        bias = rng.standard_normal(E, dtype=np.float32)
+    return lg, bias
+
+
+def _check(ids, w, o_ids, o_w):
+    got_ids = ids.cpu().numpy()
+    assert np.array_equal(got_ids, o_ids), np.argwhere(got_ids != o_ids)[:5]
+    np.testing.assert_allclose(w.cpu().numpy(), o_w, rtol=WEIGHT_RTOL, atol=0)
+
+
+# (E, k, T): per-lane width ceil(E / 64) in {1, 2, 4, 6, 8, 16}
+PLAIN = [
+    (32, 32, 77),      # k == E: every expert, in descending order
+    (33, 17, 65),      # one logit per lane, lane 32 the only one past 31
+    (64, 32, 70),
+    (65, 9, 77),       # two per lane, lane 0 alone holds a second logit
+    (96, 9, 130),
+    (96, 17, 77),
+    (128, 16, 77),
+    (128, 32, 129),
+    (256, 32, 40),
+    (384, 16, 50),
+    (385, 17, 66),     # eight per lane, mostly empty
+    (512, 9, 77),
+    (512, 17, 64),
+    (512, 32, 33),
+    (513, 16, 50),     # sixteen per lane
+    (1000, 32, 45),
+    (1024, 16, 77),
+    (1024, 32, 130),
+]
+
+
+@pytest.mark.parametrize("E,k,T", PLAIN, ids=lambda v: str(v))
+@pytest.mark.parametrize("ties", [False, True], ids=["normal", "ties"])
+def test_plain_router_at_limits(E, k, T, ties):
+    print(f"[case] plain router E={E} k={k} T={T} ties={ties}", flush=True)
+    lg, bias = _logits(T, E, ties, seed=1000 + E + 7 * k)
+    d_lg = torch.from_numpy(lg).cuda()
+    for use_bias in (False, True):
+        b = bias if use_bias else None
+        d_b = None if b is None else torch.from_numpy(b).cuda()
+        for score in (api.MOE_SCORE_SIGMOID, api.MOE_SCORE_SOFTMAX):
+            ids, w = api.moe_route_topk(d_lg, d_b, k, score)
+            torch.cuda.synchronize()
+            o_ids, o_w = oracle.route_topk(lg, b, k, score)
+            _check(ids, w, o_ids, o_w)
+
+
+# (E, groups, kept, k, T)
+GROUPED = [
+    (256, 8, 4, 16, 77),     # 8 lanes per group
+    (256, 8, 4, 32, 50),     # k == the kept groups' experts
+    (512, 8, 3, 17, 64),
+    (1024, 16, 8, 32, 45),   # 4 lanes per group, 16 logits per lane
+    (384, 8, 2, 9, 70),      # 6 logits per lane
+    (160, 8, 3, 24, 60),     # groups off whole lanes (LDS path)
+    (96, 3, 2, 17, 66),
+]
+
+
+@pytest.mark.parametrize("E,G,TG,k,T", GROUPED, ids=lambda v: str(v))
+@pytest.mark.parametrize("ties", [False, True], ids=["normal", "ties"])
+def test_grouped_router_large_k(E, G, TG, k, T, ties):
+    print(f"[case] grouped router E={E} G={G} TG={TG} k={k} T={T} ties={ties}", flush=True)
+    lg, bias = _logits(T, E, ties, seed=2000 + E + 3 * k)
+    d_lg = torch.from_numpy(lg).cuda()
+    d_b = torch.from_numpy(bias).cuda()
+    for score in (api.MOE_SCORE_SIGMOID, api.MOE_SCORE_SOFTMAX):
+        ids, w = api.moe_route_topk_grouped(d_lg, d_b, k, score, G, TG)
+        torch.cuda.synchronize()
+        o_ids, o_w = oracle.route_topk_grouped(lg, bias, k, score, G, TG)
+        _check(ids, w, o_ids, o_w)

@@ -209,6 +209,81 @@ def test_combine_f32_ordered_is_a_chain_of_fused_multiply_adds():
             assert out[t, i] == ref
 
 
+def _cancelling_terms(T, k, H, fp8, seed):
+    """Rows whose slot pairs nearly cancel (opposite signs, weights and scales
+    a few fp32 ulps apart), so each fp32 rounding in the chain reaches the
+    bf16 result; token_row = t * k + j."""
+    rng = np.random.default_rng(seed)
+    rows = T * k
+    w = rng.uniform(0.1, 0.2, size=(T, k)).astype(np.float32)
+    w[:, 1::2] = (w[:, 0::2].astype(np.float64)
+                  * (1 + rng.integers(-64, 64, size=(T, k // 2)) * 2.0 ** -23)).astype(np.float32)
+    tr = np.arange(rows, dtype=np.int32).reshape(T, k)
+    if fp8:
+        mag = rng.integers(0x38, 0x7E, size=(T, k // 2, H)).astype(np.uint8)  # 1.0 .. 448
+        codes = np.empty((T, k, H), np.uint8)
+        codes[:, 0::2] = mag
+        codes[:, 1::2] = mag | 0x80
+        ys = (np.float32(0.0123) * (1 + rng.integers(0, 1 << 12, size=(rows, H // 128))
+                                    * 2.0 ** -23)).astype(np.float32)
+        return codes.reshape(rows, H), ys, tr, w
+    v = rng.standard_normal((T, k // 2, H)).astype(np.float32)
+    y = np.empty((T, k, H), np.float32)
+    y[:, 0::2] = v
+    y[:, 1::2] = -v
+    return inputs.bf16_bits_from_f32(y.reshape(rows, H)), None, tr, w
+
+
+def test_combine_f32_ordered_fp8_is_one_rounded_product_then_fused_adds():
+    """fp8 payload: each term's value is fp32(code) * scale rounded once to
+    fp32, then folded by a fused multiply-add in slot order from 0.  Codes are
+    decoded by torch's e4m3fn cast (not the oracle's decoder) and every step
+    is exact rational arithmetic with one explicit rounding.  On rows whose
+    terms nearly cancel, the chains with the weight folded into the scale or
+    with the product left unrounded give different bf16 results, and the test
+    asserts that they do, so it tells those mistakes apart."""
+    T, k, H = 4, 8, 256
+    y, ys, tr, w = _cancelling_terms(T, k, H, fp8=True, seed=3)
+    out = oracle.combine_f32_ordered(y, ys, tr, w)
+    dec = torch.from_numpy(y).view(torch.float8_e4m3fn).double().numpy()
+    folded = unrounded = 0
+    for t in range(T):
+        for i in range(H):
+            acc = a_fold = a_unr = Fraction(0)
+            for j in range(k):
+                r = tr[t, j]
+                c, s = Fraction(float(dec[r, i])), Fraction(float(ys[r, i // 128]))
+                wj = Fraction(float(w[t, j]))
+                acc = _round_f32(wj * _round_f32(c * s) + acc)
+                a_fold = _round_f32(_round_f32(wj * s) * c + a_fold)
+                a_unr = _round_f32(wj * c * s + a_unr)
+            assert out[t, i] == oracle.f64_to_bf16(float(acc)), (t, i)
+            folded += out[t, i] != oracle.f64_to_bf16(float(a_fold))
+            unrounded += out[t, i] != oracle.f64_to_bf16(float(a_unr))
+    assert folded > 0 and unrounded > 0
+
+
+def test_combine_f32_ordered_bf16_fused_on_cancelling_rows():
+    """bf16 payload on rows whose slot pairs nearly cancel: the result is the
+    chain of fused multiply-adds (one rounding per step), and a chain of
+    separately rounded products and sums gives a different bf16 result."""
+    T, k, H = 4, 8, 256
+    y, _, tr, w = _cancelling_terms(T, k, H, fp8=False, seed=4)
+    out = oracle.combine_f32_ordered(y, None, tr, w)
+    yv = _bf16_to_f64(y)
+    unfused = 0
+    for t in range(T):
+        for i in range(H):
+            acc = a_unf = Fraction(0)
+            for j in range(k):
+                v, wj = Fraction(float(yv[tr[t, j], i])), Fraction(float(w[t, j]))
+                acc = _round_f32(wj * v + acc)
+                a_unf = _round_f32(_round_f32(wj * v) + a_unf)
+            assert out[t, i] == oracle.f64_to_bf16(float(acc)), (t, i)
+            unfused += out[t, i] != oracle.f64_to_bf16(float(a_unf))
+    assert unfused > 0
+
+
 def test_combine_skipped_pairs_add_nothing():
     inp, ids, w, lay = _case(16, 32, 8, 4, 2, 0, seed=13)
     y = oracle.dispatch_bf16(inp.x_bits, lay["token_row"], lay["rows"])
