@@ -133,6 +133,72 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+# ---------------------------------------------------------------------------
+# Argument checks made before each C call: every tensor must be a contiguous
+# GPU tensor of the expected element type holding at least the elements the
+# shape addresses (a wrong view or an undersized buffer would otherwise be
+# read or written out of bounds by the kernels).  Shapes the library rejects
+# are left to it, so its status code is what the caller sees.
+# ---------------------------------------------------------------------------
+def _gpu(t, name: str, call: str, *, dtype=None, itemsize: Optional[int] = None,
+         numel: int = 0, optional: bool = False) -> None:
+    if t is None:
+        if optional or numel == 0:
+            return
+        raise ValueError(f"{call}: {name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{call}: {name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{call}: {name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{call}: {name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{call}: {name} must be {dtype} (got {t.dtype})")
+    if itemsize is not None and t.element_size() != itemsize:
+        raise TypeError(f"{call}: {name} must have {itemsize}-byte elements (got {t.dtype})")
+    if t.numel() < numel:
+        raise ValueError(f"{call}: {name} holds {t.numel()} elements, the shape needs {numel}")
+
+
+def _rows(shape: Shape) -> Optional[int]:
+    """Receive rows of a valid shape, or None (the C call then reports it)."""
+    n = _lib.moe_recv_rows(ctypes.byref(shape.c()))
+    return None if n < 0 else int(n)
+
+
+def _payload_rows(shape: Shape, rows: int, t, ts, name: str, call: str,
+                  scales_optional: bool = False) -> None:
+    """A buffer of `rows` payload rows (bf16, or e4m3 codes plus fp32 scales)."""
+    if shape.fp8:
+        _gpu(t, name, call, itemsize=1, numel=rows * shape.hidden)
+        _gpu(ts, name + " scales", call, dtype=torch.float32,
+             numel=rows * (shape.hidden // 128), optional=scales_optional)
+    else:
+        _gpu(t, name, call, itemsize=2, numel=rows * shape.hidden)
+
+
+def _layout(lay: "Layout", shape: Shape, rows: int, call: str) -> None:
+    if lay is None:
+        raise ValueError(f"{call}: layout is required")
+    E, N = shape.num_experts, shape.num_ranks
+    for f, n in (("expert_counts", E), ("expert_offsets", E), ("rank_counts", N),
+                 ("rank_offsets", N), ("status", 1)):
+        _gpu(getattr(lay, f), "layout." + f, call, dtype=torch.int32, numel=n)
+    _gpu(lay.token_row, "layout.token_row", call, dtype=torch.int32,
+         numel=shape.num_tokens * shape.top_k)
+    _gpu(lay.row_src, "layout.row_src", call, dtype=torch.int32, numel=rows, optional=True)
+
+
+def _route_args(call, logits, bias, k, topk_ids, topk_weights):
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise ValueError(f"{call}: logits must be a 2-D tensor [T, E]")
+    T, E = logits.shape
+    _gpu(logits, "logits", call, dtype=torch.float32, numel=T * E)
+    _gpu(bias, "bias", call, dtype=torch.float32, numel=E, optional=True)
+    _gpu(topk_ids, "topk_ids", call, dtype=torch.int32, numel=T * k)
+    _gpu(topk_weights, "topk_weights", call, dtype=torch.float32, numel=T * k)
+
+
 def moe_recv_rows(shape: Shape) -> int:
     n = _lib.moe_recv_rows(ctypes.byref(shape.c()))
     if n < 0:
@@ -153,6 +219,7 @@ def moe_route_topk(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int, s
         topk_ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
     if topk_weights is None:
         topk_weights = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _route_args("moe_route_topk", logits, bias, k, topk_ids, topk_weights)
     _check(_lib.moe_route_topk(_ptr(logits), _ptr(bias), T, E, k, score, _ptr(topk_ids),
                                _ptr(topk_weights), _stream(stream)), "moe_route_topk")
     return topk_ids, topk_weights
@@ -168,6 +235,7 @@ def moe_route_topk_grouped(logits: torch.Tensor, bias: Optional[torch.Tensor], k
         topk_ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
     if topk_weights is None:
         topk_weights = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _route_args("moe_route_topk_grouped", logits, bias, k, topk_ids, topk_weights)
     _check(_lib.moe_route_topk_grouped(_ptr(logits), _ptr(bias), T, E, k, score, n_groups,
                                        topk_groups, _ptr(topk_ids), _ptr(topk_weights),
                                        _stream(stream)), "moe_route_topk_grouped")
@@ -178,6 +246,16 @@ def moe_dispatch(shape: Shape, x: torch.Tensor, topk_ids: torch.Tensor, recv_x: 
                  recv_scales: Optional[torch.Tensor], layout: Layout,
                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rows = _rows(shape)
+    if rows is not None:
+        c = "moe_dispatch"
+        T, H, k = shape.num_tokens, shape.hidden, shape.top_k
+        _gpu(x, "x", c, itemsize=2, numel=T * H)
+        _gpu(topk_ids, "topk_ids", c, dtype=torch.int32, numel=T * k)
+        _payload_rows(shape, rows, recv_x, recv_scales, "recv_x", c)
+        _layout(layout, shape, rows, c)
+        # the library compares the workspace's bytes with what the shape needs
+        _gpu(workspace, "workspace", c, optional=True)
     _check(_lib.moe_dispatch(ctypes.byref(shape.c()), _ptr(x), _ptr(topk_ids), _ptr(recv_x),
                              _ptr(recv_scales), ctypes.byref(layout.c()), _ptr(workspace),
                              ws_bytes, _stream(stream)), "moe_dispatch")
@@ -201,6 +279,19 @@ def moe_dispatch_sources(shape: Shape, num_sources: int, x: torch.Tensor,
                          workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Every source rank dispatching at once; shape holds one source's sizes."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    world = world_shape(shape, num_sources) if num_sources >= 1 else shape
+    rows = _rows(world)
+    if rows is not None and num_sources >= 1:
+        c = "moe_dispatch_sources"
+        T, H, k = world.num_tokens, world.hidden, world.top_k
+        _gpu(x, "x", c, itemsize=2, numel=T * H)
+        _gpu(topk_ids, "topk_ids", c, dtype=torch.int32, numel=T * k)
+        _payload_rows(world, rows, recv_x, recv_scales, "recv_x", c)
+        _layout(layout, world, rows, c)
+        _gpu(source_counts, "source_counts", c, dtype=torch.int32,
+             numel=num_sources * shape.num_experts)
+        _gpu(source_offsets, "source_offsets", c, dtype=torch.int32,
+             numel=num_sources * shape.num_experts)
     _check(_lib.moe_dispatch_sources(ctypes.byref(shape.c()), num_sources, _ptr(x),
                                      _ptr(topk_ids), _ptr(recv_x), _ptr(recv_scales),
                                      ctypes.byref(layout.c()), _ptr(source_counts),
@@ -211,6 +302,13 @@ def moe_dispatch_sources(shape: Shape, num_sources: int, x: torch.Tensor,
 def moe_expert_scale(shape: Shape, recv_x: torch.Tensor, recv_scales: Optional[torch.Tensor],
                      layout: Layout, alpha: torch.Tensor, y: torch.Tensor,
                      y_scales: Optional[torch.Tensor], stream=None) -> None:
+    rows = _rows(shape)
+    if rows is not None:
+        c = "moe_expert_scale"
+        _payload_rows(shape, rows, recv_x, recv_scales, "recv_x", c)
+        _payload_rows(shape, rows, y, y_scales, "y", c)
+        _gpu(alpha, "alpha", c, dtype=torch.float32, numel=shape.num_experts)
+        _layout(layout, shape, rows, c)
     _check(_lib.moe_expert_scale(ctypes.byref(shape.c()), _ptr(recv_x), _ptr(recv_scales),
                                  ctypes.byref(layout.c()), _ptr(alpha), _ptr(y), _ptr(y_scales),
                                  _stream(stream)), "moe_expert_scale")
@@ -219,6 +317,14 @@ def moe_expert_scale(shape: Shape, recv_x: torch.Tensor, recv_scales: Optional[t
 def moe_combine(shape: Shape, expert_y: torch.Tensor, expert_scales: Optional[torch.Tensor],
                 layout: Layout, topk_weights: torch.Tensor, out: torch.Tensor,
                 stream=None) -> None:
+    rows = _rows(shape)
+    if rows is not None:
+        c = "moe_combine"
+        T, H, k = shape.num_tokens, shape.hidden, shape.top_k
+        _payload_rows(shape, rows, expert_y, expert_scales, "expert_y", c)
+        _layout(layout, shape, rows, c)
+        _gpu(topk_weights, "topk_weights", c, dtype=torch.float32, numel=T * k)
+        _gpu(out, "out", c, itemsize=2, numel=T * H)
     _check(_lib.moe_combine(ctypes.byref(shape.c()), _ptr(expert_y), _ptr(expert_scales),
                             ctypes.byref(layout.c()), _ptr(topk_weights), _ptr(out),
                             _stream(stream)), "moe_combine")
@@ -240,6 +346,16 @@ def moe_combine_partial_send(shape: Shape, expert_y: torch.Tensor, expert_scales
                      layout: Layout, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
                      partial: torch.Tensor, partial_rank: torch.Tensor, stream=None) -> None:
     """Stage 1 of the two-stage combine: one bf16 row per (token, rank)."""
+    rows = _rows(shape)
+    if rows is not None:
+        c = "moe_combine_partial_send"
+        T, H, k, M = shape.num_tokens, shape.hidden, shape.top_k, partial_slots(shape)
+        _payload_rows(shape, rows, expert_y, expert_scales, "expert_y", c)
+        _layout(layout, shape, rows, c)
+        _gpu(topk_ids, "topk_ids", c, dtype=torch.int32, numel=T * k)
+        _gpu(topk_weights, "topk_weights", c, dtype=torch.float32, numel=T * k)
+        _gpu(partial, "partial", c, itemsize=2, numel=T * M * H)
+        _gpu(partial_rank, "partial_rank", c, dtype=torch.int32, numel=T * M)
     _check(_lib.moe_combine_partial_send(ctypes.byref(shape.c()), _ptr(expert_y), _ptr(expert_scales),
                                  ctypes.byref(layout.c()), _ptr(topk_ids), _ptr(topk_weights),
                                  _ptr(partial), _ptr(partial_rank), _stream(stream)),
@@ -249,6 +365,12 @@ def moe_combine_partial_send(shape: Shape, expert_y: torch.Tensor, expert_scales
 def moe_combine_partial_recv(shape: Shape, partial: torch.Tensor, partial_rank: torch.Tensor,
                      out: torch.Tensor, stream=None) -> None:
     """Stage 2: sum of each token's partial rows."""
+    if _rows(shape) is not None:
+        c = "moe_combine_partial_recv"
+        T, H, M = shape.num_tokens, shape.hidden, partial_slots(shape)
+        _gpu(partial, "partial", c, itemsize=2, numel=T * M * H)
+        _gpu(partial_rank, "partial_rank", c, dtype=torch.int32, numel=T * M)
+        _gpu(out, "out", c, itemsize=2, numel=T * H)
     _check(_lib.moe_combine_partial_recv(ctypes.byref(shape.c()), _ptr(partial), _ptr(partial_rank),
                                  _ptr(out), _stream(stream)), "moe_combine_partial_recv")
 
@@ -265,6 +387,13 @@ def moe_dispatch_recv(shape: Shape, recv_x: torch.Tensor, recv_scales: Optional[
                       layout: Layout, gemm_x: torch.Tensor, gemm_scales: Optional[torch.Tensor],
                       gemm_offsets: torch.Tensor, stream=None) -> None:
     """Receive half of dispatch: receive regions -> dense grouped-GEMM input."""
+    rows = _rows(shape)
+    if rows is not None:
+        c = "moe_dispatch_recv"
+        _payload_rows(shape, rows, recv_x, recv_scales, "recv_x", c)
+        _payload_rows(shape, shape.num_tokens * shape.top_k, gemm_x, gemm_scales, "gemm_x", c)
+        _layout(layout, shape, rows, c)
+        _gpu(gemm_offsets, "gemm_offsets", c, dtype=torch.int32, numel=shape.num_experts + 1)
     _check(_lib.moe_dispatch_recv(ctypes.byref(shape.c()), _ptr(recv_x), _ptr(recv_scales),
                                   ctypes.byref(layout.c()), _ptr(gemm_x), _ptr(gemm_scales),
                                   _ptr(gemm_offsets), _stream(stream)), "moe_dispatch_recv")
@@ -274,6 +403,12 @@ def moe_combine_send(shape: Shape, gemm_y: torch.Tensor, gemm_scales: Optional[t
                      layout: Layout, expert_y: torch.Tensor,
                      expert_scales: Optional[torch.Tensor], stream=None) -> None:
     """Send half of the combine: dense expert outputs -> receive-region layout."""
+    rows = _rows(shape)
+    if rows is not None:
+        c = "moe_combine_send"
+        _payload_rows(shape, shape.num_tokens * shape.top_k, gemm_y, gemm_scales, "gemm_y", c)
+        _payload_rows(shape, rows, expert_y, expert_scales, "expert_y", c)
+        _layout(layout, shape, rows, c)
     _check(_lib.moe_combine_send(ctypes.byref(shape.c()), _ptr(gemm_y), _ptr(gemm_scales),
                                  ctypes.byref(layout.c()), _ptr(expert_y), _ptr(expert_scales),
                                  _stream(stream)), "moe_combine_send")

@@ -181,3 +181,19 @@ def test_stream_floor_library_loads_and_rejects_bad_arguments():
     assert lib.moe_ceiling_write_blocked(4104, 16, 0, None) == 1
     assert lib.moe_ceiling_write_blocked(4096, 0, 0, None) == 1
     assert lib.moe_ceiling_write_blocked(4096, 16, 3, None) == 1
+
+
+def test_binding_refuses_host_tensors_before_the_call():
+    """The binding checks its tensors before calling the library: a host
+    (CPU) tensor where device memory is required is refused with a message
+    naming the argument."""
+    import torch
+    shape = api.Shape(4, 64, 8, 2, 2, 0)
+    with pytest.raises(ValueError, match="logits must be a GPU tensor"):
+        api.moe_route_topk(torch.zeros(4, 8), None, 2, api.MOE_SCORE_SOFTMAX,
+                           torch.zeros(4, 2, dtype=torch.int32),
+                           torch.zeros(4, 2, dtype=torch.float32))
+    with pytest.raises(ValueError, match="x must be a GPU tensor"):
+        api.moe_dispatch(shape, torch.zeros(4, 64, dtype=torch.int16),
+                         torch.zeros(4, 2, dtype=torch.int32),
+                         torch.zeros(8, 64, dtype=torch.int16), None, None)

@@ -103,3 +103,24 @@ def test_grouped_router_large_k(E, G, TG, k, T, ties):
         torch.cuda.synchronize()
         o_ids, o_w = oracle.route_topk_grouped(lg, bias, k, score, G, TG)
         _check(ids, w, o_ids, o_w)
+
+
+def test_binding_refuses_bad_views_and_types():
+    """Argument checks of the binding on the GPU: a transposed (non-contiguous)
+    logits view, int64 ids and an undersized receive buffer are refused before
+    any launch."""
+    print("[case] binding argument checks", flush=True)
+    T, E, k, H = 16, 64, 4, 256
+    lg = torch.randn(E, T, device="cuda").t()          # a [T, E] view, not contiguous
+    with pytest.raises(ValueError, match="contiguous"):
+        api.moe_route_topk(lg, None, k, api.MOE_SCORE_SIGMOID)
+    shape = api.Shape(T, H, E, k, 8, 0)
+    x = torch.zeros(T, H, dtype=torch.int16, device="cuda")
+    ids64 = torch.zeros(T, k, dtype=torch.int64, device="cuda")
+    lay = api.Layout.empty(shape, "cuda")
+    recv, _ = api.alloc_recv(shape, "cuda")
+    with pytest.raises(TypeError, match="topk_ids must be torch.int32"):
+        api.moe_dispatch(shape, x, ids64, recv, None, lay)
+    ids = torch.zeros(T, k, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="recv_x holds"):
+        api.moe_dispatch(shape, x, ids, recv[:-1], None, lay)
