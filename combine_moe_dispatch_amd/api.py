@@ -261,6 +261,30 @@ def moe_dispatch(shape: Shape, x: torch.Tensor, topk_ids: torch.Tensor, recv_x: 
                              ws_bytes, _stream(stream)), "moe_dispatch")
 
 
+_lib.moe_dispatch_static.argtypes = [ctypes.POINTER(_Shape), _vp, _vp, _vp, _vp,
+                                     ctypes.POINTER(_Layout), _vp]
+_lib.moe_dispatch_static.restype = _i32
+MOE_STATIC_SCRATCH_BYTES = 4 << 20
+
+
+def moe_dispatch_static(shape: Shape, x: torch.Tensor, topk_ids: torch.Tensor,
+                        recv_x: torch.Tensor, recv_scales: Optional[torch.Tensor],
+                        layout: Layout, stream=None) -> None:
+    """moe_dispatch without a workspace: the library's per-GPU scratch array
+    serves the multi-kernel layout path (calls on one GPU must not overlap)."""
+    rows = _rows(shape)
+    if rows is not None:
+        c = "moe_dispatch_static"
+        T, H, k = shape.num_tokens, shape.hidden, shape.top_k
+        _gpu(x, "x", c, itemsize=2, numel=T * H)
+        _gpu(topk_ids, "topk_ids", c, dtype=torch.int32, numel=T * k)
+        _payload_rows(shape, rows, recv_x, recv_scales, "recv_x", c)
+        _layout(layout, shape, rows, c)
+    _check(_lib.moe_dispatch_static(ctypes.byref(shape.c()), _ptr(x), _ptr(topk_ids),
+                                    _ptr(recv_x), _ptr(recv_scales), ctypes.byref(layout.c()),
+                                    _stream(stream)), "moe_dispatch_static")
+
+
 _lib.moe_dispatch_sources.argtypes = [ctypes.POINTER(_Shape), _i32, _vp, _vp, _vp, _vp,
                                       ctypes.POINTER(_Layout), _vp, _vp, _vp, ctypes.c_size_t,
                                       _vp]

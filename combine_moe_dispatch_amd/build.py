@@ -19,8 +19,7 @@ CEILING_LIB = os.path.join(HERE, "libmoe_ceiling.so")
 CEILING_SOURCE = "ceiling.hip"
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["capi.hip", "route_topk.hip", "dispatch.hip", "sources.hip", "combine.hip",
-           "combine_partial.hip", "gemm_io.hip",
-           "expert_scale.hip"]
+           "combine_partial.hip", "gemm_io.hip", "expert_scale.hip", "dispatch_static.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -22,6 +22,8 @@
  *  - Every pointer is a DEVICE pointer unless marked "host".  The caller
  *    allocates and owns all memory; the library allocates nothing, keeps no
  *    state between calls, and is safe to call from several host threads.
+ *    The one exception is moe_dispatch_static, whose scratch is a fixed array
+ *    the library holds in each GPU's memory (see there).
  *  - Every call enqueues its kernels on `stream` and returns without waiting;
  *    no call copies anything device-to-host, so the sequence route -> dispatch
  *    -> combine can be captured in a HIP graph.  Buffers must stay valid until
@@ -179,6 +181,28 @@ moe_status moe_dispatch(const moe_shape *shape, const void *x,
                         float *recv_scales, const moe_layout *layout,
                         void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/*
+ * moe_dispatch_static -- moe_dispatch for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments without the workspace.
+ *
+ *   Where moe_dispatch needs a workspace (moe_dispatch_workspace_size > 0),
+ *   this call uses a scratch array of MOE_STATIC_SCRATCH_BYTES that the
+ *   library holds in each GPU's memory from the first such call on that GPU
+ *   until the process ends.  It calls no allocating routine.  The current
+ *   device must be the stream's device.
+ *   Every call on one GPU shares that GPU's array: calls that may overlap on
+ *   one GPU (several streams, or several host threads) race and must be
+ *   ordered by the caller.  Nothing in the array needs clearing between calls.
+ * Errors as moe_dispatch; MOE_ERR_UNSUPPORTED (nothing launched) when the
+ * shape needs more than MOE_STATIC_SCRATCH_BYTES of workspace.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (4u << 20)
+moe_status moe_dispatch_static(const moe_shape *shape, const void *x,
+                               const int32_t *topk_ids, void *recv_x,
+                               float *recv_scales, const moe_layout *layout,
+                               hipStream_t stream);
 
 /*
  * moe_dispatch_sources -- every rank of the expert-parallel world dispatching

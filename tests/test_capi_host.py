@@ -183,6 +183,20 @@ def test_stream_floor_library_loads_and_rejects_bad_arguments():
     assert lib.moe_ceiling_write_blocked(4096, 16, 3, None) == 1
 
 
+def test_static_dispatch_rejects_what_its_scratch_cannot_hold():
+    """moe_dispatch_static refuses, before touching any device, a shape whose
+    multi-kernel layout needs more scratch than the library's array holds,
+    and rejects bad shapes like moe_dispatch."""
+    f = api._lib.moe_dispatch_static
+    good = api._Layout(16, 16, 16, 16, 16, None, 16)
+    big = api.Shape(600_000, 8, 64, 8, 8, 0)   # 4.8M pairs
+    assert api.moe_dispatch_workspace_size(big) > api.MOE_STATIC_SCRATCH_BYTES
+    assert f(ctypes.byref(big.c()), 16, 16, 16, None, ctypes.byref(good), None) == 2
+    bad = api._Shape(4, 12, 8, 2, 2, 0, 0)     # H % 8 != 0
+    assert f(ctypes.byref(bad), 16, 16, 16, None, ctypes.byref(good), None) == 1
+    assert f(None, 16, 16, 16, None, ctypes.byref(good), None) == 1
+
+
 def test_binding_refuses_host_tensors_before_the_call():
     """The binding checks its tensors before calling the library: a host
     (CPU) tensor where device memory is required is refused with a message
