@@ -1,5 +1,7 @@
 // capi.hip -- the C ABI of libmoe_dispatch.so: argument checks, then launches
 // on the caller's stream.  No allocation, no synchronisation, no state.
+#include <string.h>
+
 #include "moe_dispatch.h"
 #include "launch.h"
 
@@ -272,7 +274,12 @@ moe_status moe_combine_send(const moe_shape* shape, const void* gemm_y, const fl
 }
 
 const char* moe_status_string(moe_status status) {
-  switch (status) {
+  // A C caller may pass any int; in C++ a value outside the enumerators is
+  // not a valid moe_status, so the bits are read as an int first.
+  int code;
+  static_assert(sizeof(code) == sizeof(status), "moe_status is int-sized");
+  memcpy(&code, &status, sizeof(code));
+  switch (code) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null pointer, bad size or misaligned buffer";
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside the library's limits";

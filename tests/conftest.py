@@ -10,6 +10,8 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "sanitize: rebuilds host code with AddressSanitizer and "
+                            "UndefinedBehaviorSanitizer and runs the CPU tests against it")
     # Load what is built; build only when nothing is (hipcc cross-compiles on
     # a CPU-only host too).
     lib = os.path.join(ROOT, "combine_moe_dispatch_amd", "libmoe_dispatch.so")
