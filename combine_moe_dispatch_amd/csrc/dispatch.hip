@@ -358,6 +358,9 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   const int P = p.T * p.k;
   const int tid = threadIdx.x;
   const int lane = lane_id();
+  // the scatter blocks' arguments come with the first batch of argument
+  // loads, not a round trip after the branch below
+  MOE_ARGS_UP_FRONT("s"(p.x), "s"(p.col_chunks), "s"(p.cc_magic), "s"(p.vec_per_chunk), "s"(p.H));
 
   if (blockIdx.x == 0) {
     // histogram, scan and the global metadata; all id loads are issued
@@ -461,8 +464,10 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
     }
   }
   row = checked_row(p, row);
-  publish_rows(p, t, cc, row);
+  // payload first: the metadata stores come after it, so the wait for the x
+  // slice before the payload stores is not also a wait for them
   store_slice<PAYLOAD, MAXV>(p, u0, u1, xv, row);
+  publish_rows(p, t, cc, row);
 }
 
 // ---------------------------------------------------------------------------
@@ -604,8 +609,10 @@ __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams
     }
   }
   row = checked_row(p, row);
-  publish_rows(p, t, cc, row);
+  // payload first: the metadata stores come after it, so the wait for the x
+  // slice before the payload stores is not also a wait for them
   store_slice<PAYLOAD, MAXV>(p, u0, u1, xv, row);
+  publish_rows(p, t, cc, row);
 }
 
 static_assert(kSmallMaxPairs <= 16 * kBlock, "the fused path loads at most 16 ids per thread");

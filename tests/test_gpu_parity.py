@@ -89,6 +89,8 @@ SWEEP = [
     (700, 20480, 64, 8, 8, 0, 0, False, 1),        # wide rows on the chunked path
     (600, 2048, 1024, 8, 64, 0, 1, True, None),    # fp8, E at the library maximum, chunked
     (100, 1024, 512, 32, 16, 3200, 1, False, 3),   # fp8, k at the library maximum, repeats
+    (70000, 8, 4, 2, 2, 0, 0, True, None),         # more tokens than a grid's y dimension holds
+    (5000, 16, 8, 2, 2, 0, 0, False, None),        # combine grid just past 8192 blocks
 ]
 
 
