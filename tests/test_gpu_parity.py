@@ -89,6 +89,10 @@ SWEEP = [
     (700, 20480, 64, 8, 8, 0, 0, False, 1),        # wide rows on the chunked path
     (600, 2048, 1024, 8, 64, 0, 1, True, None),    # fp8, E at the library maximum, chunked
     (100, 1024, 512, 32, 16, 3200, 1, False, 3),   # fp8, k at the library maximum, repeats
+    # near the one-kernel limit with many blocks per compute unit: odd T,
+    # repeated experts, rows of two chunks; fp8 with capacity overflow
+    (999, 4104, 64, 4, 8, 0, 0, False, 3),
+    (1021, 256, 32, 4, 4, 1100, 1, False, 2),
     (70000, 8, 4, 2, 2, 0, 0, True, None),         # more tokens than a grid's y dimension holds
     (5000, 16, 8, 2, 2, 0, 0, False, None),        # combine grid just past 8192 blocks
 ]
