@@ -81,6 +81,10 @@ def parse():
     ap.add_argument("--write-dir")
     ap.add_argument("--cal-fetch-dir")
     ap.add_argument("--cal-write-dir")
+    ap.add_argument("--bench-json",
+                    help="with --summarize-profile: the bench.py line of a run without the "
+                         "profiler on the same sources (its algorithmic bytes and event timings "
+                         "are compared with the profile)")
     ap.add_argument("--write-figures", action="store_true",
                     help="with --summarize-profile: also write profiles/figures_<options>.txt")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -583,9 +587,15 @@ def summarize_profile(args):
     from combine_moe_dispatch_amd import inputs
     w = inputs.WORKLOADS[args.workload]
     nb = algorithmic_bytes(w)
+    line = None
+    if args.bench_json:
+        with open(args.bench_json) as f:
+            line = json.loads([x for x in f.read().splitlines() if x.strip()][-1])
+        nb.update({k: v for k, v in line["algorithmic_bytes"].items() if k in nb})
     tag = profile_tag(args)
     out = []
     figures = {}
+    parts_us = {}
     # kernel trace: per kernel, every dispatch's end - start
     rows = _csv_rows(args.trace_dir, "kernel_trace.csv")
     durs = {}
@@ -615,11 +625,27 @@ def summarize_profile(args):
             continue
         med = sum(float(np.median(d)) for _, d in ks) / 1e3
         mean = sum(float(np.mean(d)) for _, d in ks) / 1e3
+        parts_us[part] = (med, mean)
         gbs = nb[part] / (med * 1e-6) / 1e9
         figures[f"{part}_rocprof_median_us"] = f"{med:.3f}"
         figures[f"{part}_rocprof_mean_us"] = f"{mean:.3f}"
         out.append(f"| {part} | {', '.join(f for f, _ in ks)} | {med:.3f} | {mean:.3f} | "
                    f"{nb[part]} | {gbs:.0f} | {gbs / HBM_PEAK_GBS:.4f} |")
+    if line is not None:
+        ev = {"route": line["route_us"], "dispatch": line["dispatch_us"],
+              "combine": line["combine_us"]}
+        out.append("")
+        out.append("Event timing of the same sources without the profiler (per launch, graph "
+                   "difference method) against the profiled kernel durations:")
+        out.append("")
+        out.append("| step part | bench.py us per launch | rocprofv3 median us | median / event | "
+                   "rocprofv3 mean us | mean / event |")
+        out.append("|---|---|---|---|---|---|")
+        for part in ("route", "dispatch", "combine"):
+            if part in parts_us:
+                med, mean = parts_us[part]
+                out.append(f"| {part} | {ev[part]:.3f} | {med:.3f} | {med / ev[part]:.3f} | "
+                           f"{mean:.3f} | {mean / ev[part]:.3f} |")
     # counters, scaled by what the same counter reads for a copy of known size
     if args.fetch_dir and args.write_dir and args.cal_fetch_dir and args.cal_write_dir:
         def per_kernel(directory, counter):

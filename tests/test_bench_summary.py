@@ -1,0 +1,68 @@
+"""bench.py --summarize-profile on small synthetic rocprofv3 outputs (CPU):
+medians and means of the kernel trace per step part, the copy calibration
+of FETCH_SIZE / WRITE_SIZE, the traffic ratio against the algorithmic bytes
+of the bench line, and the figures file bench.py reads back."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _write(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(header)
+        wr.writerows(rows)
+
+
+def test_profile_summary(tmp_path):
+    kt = tmp_path / "kt"
+    names = {"route": "void moe::(anonymous namespace)::route_topk_kernel<4, false>(float const*)",
+             "dispatch": "void moe::(anonymous namespace)::dispatch_fused_kernel<0, 2, 4, 2>(moe::P)",
+             "combine": "void moe::(anonymous namespace)::combine_bf16_kernel<8, false>(int)"}
+    durs = {"route": [3000, 3100, 3200], "dispatch": [4000, 4200, 4400, 9000],
+            "combine": [4100, 4300, 4500]}
+    rows, t = [], 1000
+    for part, ds in durs.items():
+        for d in ds:
+            rows.append(["KERNEL_DISPATCH", names[part], t, t + d])
+            t += d + 500
+    _write(str(kt / "host" / "run_kernel_trace.csv"),
+           ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    cc_header = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    gib_kib = float(1 << 20)
+    _write(str(tmp_path / "calf" / "run_counter_collection.csv"), cc_header,
+           [["__amd_rocclr_copyBuffer", "FETCH_SIZE", gib_kib / 2]] * 5)
+    _write(str(tmp_path / "calw" / "run_counter_collection.csv"), cc_header,
+           [["__amd_rocclr_copyBuffer", "WRITE_SIZE", gib_kib]] * 5)
+    _write(str(tmp_path / "fetch" / "run_counter_collection.csv"), cc_header,
+           [[names["dispatch"], "FETCH_SIZE", 900.0], [names["combine"], "FETCH_SIZE", 7000.0],
+            [names["route"], "FETCH_SIZE", 70.0]])
+    _write(str(tmp_path / "write" / "run_counter_collection.csv"), cc_header,
+           [[names["dispatch"], "WRITE_SIZE", 14000.0], [names["combine"], "WRITE_SIZE", 1750.0],
+            [names["route"], "WRITE_SIZE", 8.0]])
+    nb = {"route": 100000, "dispatch": 16000000, "combine": 17000000}
+    (tmp_path / "bench.json").write_text(json.dumps(
+        {"algorithmic_bytes": nb, "route_us": 3.0, "dispatch_us": 4.0, "combine_us": 4.3}) + "\n")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-profile",
+                        "--workload", "dsv3_decode", "--trace-dir", str(kt),
+                        "--fetch-dir", str(tmp_path / "fetch"), "--write-dir",
+                        str(tmp_path / "write"), "--cal-fetch-dir", str(tmp_path / "calf"),
+                        "--cal-write-dir", str(tmp_path / "calw"),
+                        "--bench-json", str(tmp_path / "bench.json")],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    out = r.stdout
+    # dispatch median of 4000, 4200, 4400, 9000 ns is 4.3 us; mean 5.4 us
+    assert "| dispatch | dispatch_fused_kernel | 4.300 | 5.400 | 16000000 |" in out
+    assert "FETCH_SIZE x 2.0000, WRITE_SIZE x 1.0000" in out
+    # dispatch traffic: (900 * 2 + 14000) KiB
+    assert f"| dispatch | {1024 * (900 * 2 + 14000):.0f} | 16000000 |" in out
+    # event comparison: combine median 4.3 us against 4.3 us per launch
+    assert "| combine | 4.300 | 4.300 | 1.000 |" in out
