@@ -85,9 +85,16 @@ moe_status moe_route_topk_grouped(const float* logits, const float* bias, int32_
                                          topk_ids, topk_weights, stream));
 }
 
-moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids,
-                        void* recv_x, float* recv_scales, const moe_layout* layout,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// moe_dispatch, and with S > 0 the per-source metadata of moe_dispatch_sources
+// written by the scatter launch of the multi-kernel path (the caller has
+// checked that every chunk lies inside one source).
+moe_status dispatch_impl(const moe_shape* shape, const void* x, const int32_t* topk_ids,
+                         void* recv_x, float* recv_scales, const moe_layout* layout,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream, int S,
+                         int chunks_per_source, int32_t* source_counts,
+                         int32_t* source_offsets) {
   int L;
   int64_t rows;
   moe_status st = check_shape(shape, &L, &rows);
@@ -125,7 +132,20 @@ moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* to
   p.L = L;
   p.C = shape->rank_capacity;
   p.payload = fp8 ? 1 : 0;
+  p.src_S = S;
+  p.src_cps = chunks_per_source;
+  p.src_counts = source_counts;
+  p.src_offsets = source_offsets;
   return from_hip(moe::launch_dispatch(p, stream));
+}
+
+}  // namespace
+
+moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids,
+                        void* recv_x, float* recv_scales, const moe_layout* layout,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return dispatch_impl(shape, x, topk_ids, recv_x, recv_scales, layout, workspace,
+                       workspace_bytes, stream, 0, 0, nullptr, nullptr);
 }
 
 moe_status moe_dispatch_sources(const moe_shape* shape, int32_t num_sources, const void* x,
@@ -143,14 +163,14 @@ moe_status moe_dispatch_sources(const moe_shape* shape, int32_t num_sources, con
   moe_status st = check_shape(&world, &L, &rows);
   if (st != MOE_OK) return st;
   if (!source_counts || !source_offsets) return MOE_ERR_INVALID_ARG;
+  if (moe::dispatch_bases_per_source(num_sources, shape->num_tokens, shape->top_k))
+    return dispatch_impl(&world, x, topk_ids, recv_x, recv_scales, layout, workspace,
+                         workspace_bytes, stream, num_sources,
+                         shape->num_tokens * shape->top_k / moe::kChunkPairs, source_counts,
+                         source_offsets);
   st = moe_dispatch(&world, x, topk_ids, recv_x, recv_scales, layout, workspace, workspace_bytes,
                     stream);
   if (st != MOE_OK) return st;
-  if (moe::dispatch_bases_per_source(num_sources, shape->num_tokens, shape->top_k))
-    return from_hip(moe::launch_source_from_bases(
-        moe::dispatch_chunk_bases(workspace, world.num_tokens, shape->top_k), num_sources,
-        shape->num_tokens, shape->top_k, shape->num_experts, layout->expert_counts,
-        layout->expert_offsets, source_counts, source_offsets, stream));
   return from_hip(moe::launch_source_metadata(topk_ids, num_sources, shape->num_tokens,
                                               shape->top_k, shape->num_experts,
                                               layout->expert_offsets, source_counts,

@@ -576,9 +576,39 @@ __global__ void __launch_bounds__(kBlock) layout_scan_kernel(DispatchParams p) {
   write_metadata(p, s_cnt, s_excl, bad);
 }
 
-// Chunked path, kernel 3: rows from the chunk bases, then the scatter.
+// Sources dispatching at once, every chunk inside one source: the base of
+// source s's first chunk for expert e counts e's ids in the sources before s,
+// so source s's block of expert e begins at expert_offsets[e] plus that base
+// and holds the difference to the next source's base (the expert's total
+// after the last source).  One wave per expert, lanes over sources.
+__device__ __forceinline__ void source_metadata_from_bases(const DispatchParams& p, unsigned b) {
+  const int e = (int)b * kWaves + (int)threadIdx.x / kWave;
+  if (e >= p.E) return;  // whole wave
+  const int lane = lane_id();
+  const int off = p.expert_offsets[e];
+  const int total = p.expert_counts[e];
+  const size_t stride = (size_t)p.src_cps * p.E;
+  for (int s0 = 0; s0 < p.src_S; s0 += kWave) {
+    const int s = s0 + lane;
+    const int b0 = s < p.src_S ? p.chunk_hist[(size_t)s * stride + e] : 0;
+    const int b1 = s + 1 < p.src_S ? p.chunk_hist[(size_t)(s + 1) * stride + e] : total;
+    if (s < p.src_S) {
+      p.src_offsets[(size_t)e * p.src_S + s] = off + b0;
+      p.src_counts[(size_t)s * p.E + e] = b1 - b0;
+    }
+  }
+}
+
+// Chunked path, kernel 3: rows from the chunk bases, then the scatter (and,
+// for sources dispatching at once, the per-source metadata in the blocks past
+// the scatter's).
 template <int PAYLOAD, int MAXV>
 __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams p) {
+  const unsigned scatter_blocks = (unsigned)p.T * (unsigned)p.col_chunks;
+  if (blockIdx.x >= scatter_blocks) {
+    source_metadata_from_bases(p, blockIdx.x - scatter_blocks);
+    return;
+  }
   const int t = (int)udiv_magic(blockIdx.x, (uint32_t)p.col_chunks, p.cc_magic);
   const int cc = blockIdx.x - t * p.col_chunks;
   const int u0 = cc * p.vec_per_chunk;
@@ -652,7 +682,8 @@ hipError_t launch_paths(const DispatchParams& p, hipStream_t st) {
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((dispatch_scatter_kernel<PAYLOAD, MAXV>),
-                     dim3((unsigned)p.T * (unsigned)p.col_chunks), dim3(kBlock), 0, st, p);
+                     dim3((unsigned)p.T * (unsigned)p.col_chunks + (unsigned)p.src_blocks),
+                     dim3(kBlock), 0, st, p);
   return hipGetLastError();
 }
 
@@ -672,12 +703,6 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 bool dispatch_bases_per_source(int S, int T, int k) {
   const long P = (long)S * T * k;
   return S > 1 && P > kSmallMaxPairs && ((long)T * k) % kChunkPairs == 0;
-}
-
-const int32_t* dispatch_chunk_bases(const void* workspace, int total_tokens, int k) {
-  const size_t P = (size_t)total_tokens * (size_t)k;
-  return reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(workspace) +
-                                          align256(4 * P));
 }
 
 size_t dispatch_workspace_bytes(int T, int k, int E) {
@@ -722,6 +747,10 @@ hipError_t launch_dispatch(const DispatchParams& in, hipStream_t st) {
     ws += align256(4 * (size_t)p.nchunks * p.E);
     p.chunk_bad = reinterpret_cast<int32_t*>(ws);
   }
+  // the source metadata comes only with the chunked path's scatter
+  p.src_blocks = P > (size_t)kSmallMaxPairs && p.src_S > 1 && p.src_counts && p.src_offsets
+                     ? (p.E + kWaves - 1) / kWaves
+                     : 0;
   return p.payload == 0 ? launch_payload<0>(p, st) : launch_payload<1>(p, st);
 }
 

@@ -37,6 +37,15 @@ struct DispatchParams {
   int vec_per_chunk;  // row units per block (8 columns bf16, 16 columns fp8)
   uint32_t l_magic;   // ceil(2^32 / L) for L >= 2: e / L == umulhi(e, l_magic) for e < 2^16
   uint32_t cc_magic;  // udiv_magic_of(col_chunks)
+  // Sources dispatching at once (moe_dispatch_sources) on the multi-kernel
+  // path, every chunk inside one source: src_blocks extra blocks at the end of
+  // the scatter grid read the per-source metadata off the chunk bases (one
+  // wave per expert).  src_blocks == 0 otherwise.
+  int src_S;    // number of sources
+  int src_cps;  // chunks per source
+  int src_blocks;
+  int32_t* src_counts;   // [S][E]
+  int32_t* src_offsets;  // [E][S]
 };
 
 size_t dispatch_workspace_bytes(int T, int k, int E);
@@ -47,13 +56,9 @@ hipError_t launch_route_topk(const float* logits, const float* bias, int T, int 
                              hipStream_t st);
 
 // Multi-kernel dispatch over S sources of T tokens whose chunks each lie
-// inside one source; its chunk bases then give the per-source metadata.
+// inside one source; its chunk bases then give the per-source metadata, which
+// the scatter launch writes when DispatchParams::src_* are set.
 bool dispatch_bases_per_source(int S, int T, int k);
-const int32_t* dispatch_chunk_bases(const void* workspace, int total_tokens, int k);
-hipError_t launch_source_from_bases(const int32_t* chunk_base, int S, int T, int k, int E,
-                                    const int32_t* expert_counts, const int32_t* expert_offsets,
-                                    int32_t* source_counts, int32_t* source_offsets,
-                                    hipStream_t st);
 
 hipError_t launch_source_metadata(const int32_t* ids, int S, int T, int k, int E,
                                   const int32_t* expert_offsets, int32_t* source_counts,
