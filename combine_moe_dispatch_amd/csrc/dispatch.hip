@@ -31,7 +31,9 @@
 //    pair's rank among equal experts inside the chunk (wave ballot matching,
 //    no atomics on the placement path) and the chunk's histogram; (2) one
 //    block turns the chunk histograms into per-chunk bases and the global
-//    metadata; (3) the scatter reads a pair's row from those.
+//    metadata; (3) the scatter reads a pair's row from those (for sources
+//    dispatching at once with every chunk inside one source, blocks past the
+//    scatter's also write the per-source counts and offsets).
 //
 // Rows move as 16-byte vectors with non-temporal (streaming) hints.  With the
 // fp8 payload a lane owns 16 columns and each group of 8 lanes one 128-column
