@@ -402,11 +402,64 @@ def run_gpu(args, w, inp):
         if cold and grouping is not None:
             r["route_grouped"] = timer.per_launch(on(route_grouped, sr), sr, K)
         res[mode] = r
+    if not args.no_floor and w.payload == "bf16" and w.sources == 1:
+        res["dispatch_shape"] = dispatch_shape_floor(torch, stream, timer, w, sets[:s_disp], K)
     del sets
     torch.cuda.empty_cache()
     if not args.no_floor:
         res["floor"] = stream_floor(torch, stream, timer, payload_bytes(w), K)
     return res
+
+
+def dispatch_columns(w):
+    """(column chunks per token, 16-byte vectors per chunk) of the bf16
+    dispatch's scatter grid, by its launcher's rule: on the one-launch path
+    (T*k <= 4096) up to two vectors per thread of a 256-thread block but no
+    fewer chunks than give each of the 256 compute units a block, otherwise one
+    vector per thread; chunks are whole multiples of 128 columns."""
+    nunits = w.H // 8
+    ceil = lambda a, b: -(-a // b)
+    if w.tokens * w.k <= 4096:
+        cc = max(ceil(nunits, 512), min(ceil(256, max(w.tokens, 1)), ceil(nunits, 256)))
+    else:
+        cc = ceil(nunits, 256)
+    vpc = ceil(ceil(nunits, cc), 16) * 16
+    return ceil(nunits, vpc), vpc
+
+
+def dispatch_shape_floor(torch, stream, timer, w, sets, K):
+    """The bf16 dispatch's data movement without the row derivation, one part
+    at a time, on the dispatch's own grid (libmoe_ceiling's rows-copy kernel)
+    and the same rotating sets: a constant stored to rows t*k+j (one contiguous
+    region), the same after reading each token's x slice, a constant stored to
+    the rows of the layout the dispatch wrote (its rank regions), and x copied
+    to those rows -- what a dispatch that is handed its rows would take."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "combine_moe_dispatch_amd", "libmoe_ceiling.so"))
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.moe_ceiling_rows_copy.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    cc, vpc = dispatch_columns(w)
+    nvec = w.H // 8
+    rows_total = w.N * w.C if w.C > 0 else w.tokens * w.k
+    S = len(sets)
+    st = stream.cuda_stream
+
+    def timed(with_x, with_rows):
+        def launch(i):
+            s = sets[i % S]
+            rc = lib.moe_ceiling_rows_copy(s.x.data_ptr() if with_x else None,
+                                           s.lay.token_row.data_ptr() if with_rows else None,
+                                           s.recv.data_ptr(), w.tokens, w.k, nvec, cc, vpc,
+                                           rows_total, st)
+            assert rc == 0, rc
+        return timer.per_launch(launch, S, K)["us"]
+
+    # the first timing of a kernel of this library in a process reads high
+    # (measured 3.9 against 3.3 us at DeepSeek-V3 decode): one discarded pass
+    timed(False, False)
+    return {"column_chunks": cc, "fill_dense_us": timed(False, False),
+            "copy_dense_us": timed(True, False), "fill_rows_us": timed(False, True),
+            "copy_rows_us": timed(True, True)}
 
 
 def two_stage_bytes(w, partial_rows):
@@ -836,6 +889,12 @@ def main():
             "write_plus_read_us": round(fl["write_us"] + fl["read_us"], 3),
             "dispatch_over_write_floor": round(us["dispatch"] / fl["write_us"], 3),
             "combine_over_read_floor": round(us["combine"] / fl["read_us"], 3)}
+        if "dispatch_shape" in g:
+            ds = g["dispatch_shape"]
+            line["stream_floor"]["dispatch_shape"] = {
+                "column_chunks": ds["column_chunks"],
+                **{k: round(v, 3) for k, v in ds.items() if k.endswith("_us")},
+                "dispatch_over_copy_rows": round(us["dispatch"] / ds["copy_rows_us"], 3)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

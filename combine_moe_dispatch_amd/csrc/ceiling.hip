@@ -1,7 +1,7 @@
 // ceiling.hip -- plain streaming kernels that measure what this GPU's memory
 // system sustains at a given size: read, write and copy of a buffer with the
-// same 16-byte non-temporal accesses the dispatch and combine kernels use, and
-// an empty launch.  They are the measured floor against which the MoE
+// same 16-byte non-temporal accesses the dispatch and combine kernels use, an
+// empty launch, and the dispatch's own row copy with its rows handed to it.  They are the measured floor against which the MoE
 // kernels' times are judged (libmoe_ceiling.so, used by the benchmark only;
 // not part of the dispatch/combine interface).
 #include <hip/hip_runtime.h>
@@ -58,6 +58,43 @@ stream_copy_kernel(const u32x4* __restrict__ s, u32x4* __restrict__ d, size_t n)
     __builtin_nontemporal_store(__builtin_nontemporal_load(&s[i]), &d[i]);
 }
 
+// The dispatch's data movement with its rows handed to it: block b owns
+// (token b / col_chunks, column chunk b % col_chunks) of vpc 16-byte vectors,
+// at most two per thread, and stores its slice of x row t (a constant when x
+// is null) to the k rows listed for t in rows (row t*k + j when rows is
+// null), with the dispatch's 16-byte non-temporal loads and stores.  Rows
+// outside [0, rows_total) are skipped.  What a dispatch that did not have to
+// derive its rows would take, one part at a time.
+__global__ void __launch_bounds__(256)
+rows_copy_kernel(const u32x4* __restrict__ x, const int* __restrict__ rows,
+                 u32x4* __restrict__ dst, int k, int nvec, int col_chunks, int vpc,
+                 int rows_total) {
+  const int t = (int)blockIdx.x / col_chunks;
+  const int cc = (int)blockIdx.x - t * col_chunks;
+  const int u0 = cc * vpc;
+  const int u1 = min(u0 + vpc, nvec);
+  const int slot = min((int)(threadIdx.x & 63), k - 1);
+  const int row_lane = rows ? rows[(size_t)t * k + slot] : t * k + slot;
+  u32x4 xv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = u0 + (int)threadIdx.x + i * 256;
+    if (x)
+      xv[i] = __builtin_nontemporal_load(&x[(size_t)t * nvec + min(u, u1 - 1)]);
+    else
+      xv[i] = (u32x4){(unsigned)t, (unsigned)u, 0u, 0u};
+  }
+  for (int j = 0; j < k; ++j) {
+    const int row = __builtin_amdgcn_readlane(row_lane, j);
+    if (row < 0 || row >= rows_total) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = u0 + (int)threadIdx.x + i * 256;
+      if (u < u1) __builtin_nontemporal_store(xv[i], &dst[(size_t)row * nvec + u]);
+    }
+  }
+}
+
 __global__ void empty_kernel() {}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -105,6 +142,23 @@ extern "C" int moe_ceiling_copy(const void* src, void* dst, size_t nvec, int blo
     return 1;
   hipLaunchKernelGGL(stream_copy_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), nvec);
+  return (int)hipGetLastError();
+}
+
+// x: [T][nvec] 16-byte vectors or null (a constant is stored); rows: [T][k]
+// or null (rows t*k + j); dst: [rows_total][nvec].  Blocks T * col_chunks;
+// col_chunks * vpc must cover nvec with vpc <= 512 (two vectors per thread).
+extern "C" int moe_ceiling_rows_copy(const void* x, const int32_t* rows, void* dst, int T, int k,
+                                     int nvec, int col_chunks, int vpc, int rows_total,
+                                     hipStream_t stream) {
+  if (!dst || !aligned16(dst) || (x && !aligned16(x)) || T < 1 || k < 1 || k > 64 ||
+      nvec < 1 || col_chunks < 1 || vpc < 1 || vpc > 512 ||
+      (long long)col_chunks * vpc < nvec || rows_total < 1 ||
+      (long long)T * col_chunks > 0x7fffffffLL || (!rows && (long long)T * k > rows_total))
+    return 1;
+  hipLaunchKernelGGL(rows_copy_kernel, dim3((unsigned)(T * col_chunks)), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(x), rows, static_cast<u32x4*>(dst), k, nvec,
+                     col_chunks, vpc, rows_total);
   return (int)hipGetLastError();
 }
 

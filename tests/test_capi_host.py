@@ -181,6 +181,31 @@ def test_stream_floor_library_loads_and_rejects_bad_arguments():
     assert lib.moe_ceiling_write_blocked(4104, 16, 0, None) == 1
     assert lib.moe_ceiling_write_blocked(4096, 0, 0, None) == 1
     assert lib.moe_ceiling_write_blocked(4096, 16, 3, None) == 1
+    # the dispatch-shaped copy: (x, rows, dst, T, k, nvec, col_chunks, vpc, rows_total)
+    rc = lib.moe_ceiling_rows_copy
+    rc.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    assert rc(4096, None, None, 4, 2, 64, 1, 64, 8, None) == 1      # no destination
+    assert rc(4104, None, 4096, 4, 2, 64, 1, 64, 8, None) == 1      # misaligned x
+    assert rc(4096, None, 4096, 4, 65, 64, 1, 64, 260, None) == 1   # k past a wave
+    assert rc(4096, None, 4096, 4, 2, 1024, 1, 1024, 8, None) == 1  # vpc past two per thread
+    assert rc(4096, None, 4096, 4, 2, 600, 1, 512, 8, None) == 1    # chunks miss columns
+    assert rc(4096, None, 4096, 4, 2, 64, 1, 64, 7, None) == 1      # rows t*k+j past the end
+    assert rc(4096, None, 4096, 0, 2, 64, 1, 64, 8, None) == 1      # no tokens
+
+
+def test_dispatch_columns_follow_the_launcher_rule():
+    """bench.py's copy of the bf16 dispatch's column split: two chunks of 448
+    vectors at 128 tokens (256 blocks for 256 compute units), one vector per
+    thread past the one-launch limit, whole 128-column chunks."""
+    import bench
+    from combine_moe_dispatch_amd import inputs
+    W = inputs.WORKLOADS
+    assert bench.dispatch_columns(W["dsv3_decode"]) == (2, 448)
+    assert bench.dispatch_columns(W["skewed_prefill"]) == (4, 224)
+    assert bench.dispatch_columns(W["tiny"]) == (1, 32)
+    for w in W.values():
+        cc, vpc = bench.dispatch_columns(w)
+        assert vpc % 16 == 0 and cc * vpc >= w.H // 8 > (cc - 1) * vpc and vpc <= 512
 
 
 def test_static_dispatch_rejects_what_its_scratch_cannot_hold():
