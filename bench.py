@@ -89,6 +89,12 @@ def parse():
                     help="with --summarize-profile: also write profiles/figures_<options>.txt")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (PMC scale factor)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="instead of the benchmark: phase timeline of the one-launch dispatch "
+                         "and the bf16 combine from libmoe_trace.so (the same sources with "
+                         "phase stamps), on rotating cold buffer sets; one JSON line")
+    ap.add_argument("--launches", type=int, default=0,
+                    help="with --timeline: launches read back per kernel (0 = twice the sets)")
     return ap.parse_args()
 
 
@@ -409,6 +415,141 @@ def run_gpu(args, w, inp):
     if not args.no_floor:
         res["floor"] = stream_floor(torch, stream, timer, payload_bytes(w), K)
     return res
+
+
+# names of the phase stamps in a trace record (words 0-5)
+TRACE_PHASES = {
+    "dispatch": ["entry", "lds_cleared", "histogram", "rows_known", "stores_issued",
+                 "stores_done"],
+    "combine": ["entry", "gathers_issued", "folded", "folded_", "store_issued", "store_done"],
+}
+
+
+def timeline_summary(recs, phases, first_slots=0):
+    """Per-phase 10th/50th/90th percentile and maximum, in us from the launch's
+    earliest entry, pooled over launches.  recs: [launches][slots][8] int64
+    trace records (word 7 = 1 when written); the first `first_slots` slots of
+    each launch (the dispatch's metadata block) are reported apart, by their
+    entry and completion only."""
+    import numpy as np
+    out, meta = {}, []
+    per_phase = {p: [] for p in phases if not p.endswith("_")}
+    spans = []
+    for r in recs:
+        ok = r[:, 7] == 1
+        if not ok.any():
+            continue
+        base = r[ok, 0].min()
+        t = (r[:, :6] - base) * 0.01   # 100 MHz clock: ticks of 10 ns
+        body = ok.copy()
+        body[:first_slots] = False
+        for i, p in enumerate(phases):
+            if p in per_phase:
+                per_phase[p].append(t[body, i])
+        if first_slots:
+            meta.append(t[:first_slots][ok[:first_slots]][:, [0, 5]])
+        spans.append(t[ok, 5].max())
+    for p, v in per_phase.items():
+        a = np.concatenate(v)
+        out[p] = {"p10": round(float(np.percentile(a, 10)), 3),
+                  "p50": round(float(np.percentile(a, 50)), 3),
+                  "p90": round(float(np.percentile(a, 90)), 3),
+                  "max": round(float(a.max()), 3)}
+    res = {"phases_us": out, "last_done_us_p50": round(float(np.median(spans)), 3),
+           "records_per_launch": int(np.median([int((r[:, 7] == 1).sum()) for r in recs]))}
+    if meta:
+        m = np.concatenate(meta)
+        res["metadata_block_us"] = {"entry_p50": round(float(np.median(m[:, 0])), 3),
+                                    "done_p50": round(float(np.median(m[:, 1])), 3),
+                                    "done_max": round(float(m[:, 1].max()), 3)}
+    return res
+
+
+def run_timeline(args, w, inp):
+    """Phase timeline of the one-launch dispatch (fused kernel, bf16 or fp8)
+    and the bf16 combine, read from libmoe_trace.so -- the library's own sources compiled
+    with -DMOE_PHASE_STAMPS, whose kernels record the 100 MHz wall clock at
+    each phase of their path (the product library holds none of this).  The
+    launches run back to back in HIP graphs that rotate over as many buffer
+    sets as the timed graphs use, and the last launch of each replay is read
+    back (cold, like every timed launch).  The stamps' own waits and stores
+    add about 0.2 us, so the times locate the phases rather than time the
+    kernels."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from combine_moe_dispatch_amd import api
+    if w.sources != 1 or w.tokens * w.k > 4096:
+        return {"timeline": None,
+                "reason": "the trace covers the one-launch dispatch (T*k <= 4096, one "
+                          "source) and the bf16 combine"}
+    fp8 = w.payload == "fp8"
+    lib = ctypes.CDLL(os.path.join(ROOT, "combine_moe_dispatch_amd", "libmoe_trace.so"))
+    for name in ("moe_route_topk", "moe_dispatch", "moe_expert_scale", "moe_combine",
+                 "moe_recv_rows", "moe_dispatch_workspace_size", "moe_status_string"):
+        f, g = getattr(lib, name), getattr(api._lib, name)
+        f.argtypes, f.restype = g.argtypes, g.restype
+    vp, u32 = ctypes.c_void_p, ctypes.c_uint32
+    lib.moe_trace_set_dispatch.argtypes = [vp, u32]
+    lib.moe_trace_set_combine.argtypes = [vp, u32]
+    api._lib = lib   # this process's binding calls now go to the tracing library
+    torch.cuda.set_device(0)
+    shape = api.Shape(w.T, w.H, w.E, w.k, w.N, w.C,
+                      api.MOE_PAYLOAD_FP8_E4M3_B128 if fp8 else api.MOE_PAYLOAD_BF16)
+    S = max(sets_for(algorithmic_bytes(w)["dispatch"], args.sets or 64),
+            sets_for(algorithmic_bytes(w)["combine"], args.sets or 64))
+    sets = [BufferSet(api, w, shape, inp, torch, np) for _ in range(S)]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for s in sets:
+            api.moe_route_topk(s.logits, s.bias, w.k, w.score, s.ids, s.w, stream=stream)
+            api.moe_dispatch(shape, s.x, s.ids, s.recv, s.rs, s.lay, s.ws, stream=stream)
+            api.moe_expert_scale(shape, s.recv, s.rs, s.lay, s.alpha, s.y, s.ys, stream=stream)
+    stream.synchronize()
+    nvec = w.H // 8
+    d_slots = (1 + w.tokens * -(-nvec // 256)) * 4     # the fused grid's waves, at most
+    # (fp8: 16 columns a unit, so fewer blocks than this bound)
+    c_slots = w.tokens * -(-nvec // 64)                 # one-wave combine blocks
+    d_buf = torch.zeros(d_slots * 8, dtype=torch.int64, device="cuda")
+    c_buf = torch.zeros(c_slots * 8, dtype=torch.int64, device="cuda")
+    assert lib.moe_trace_set_dispatch(d_buf.data_ptr(), d_slots) == 0
+    assert lib.moe_trace_set_combine(c_buf.data_ptr(), c_slots) == 0
+    # a graph of S back-to-back launches, one per set: each launch's records
+    # overwrite the previous one's, so after a replay the buffer holds the
+    # last launch's (on set S-1, cold: S launches have passed since it was
+    # last used); each replay gives one launch
+    timer = GraphTimer(torch, stream, 1)
+    graphs = {
+        "dispatch": (timer.capture(lambda i: api.moe_dispatch(
+            shape, sets[i].x, sets[i].ids, sets[i].recv, sets[i].rs, sets[i].lay, sets[i].ws,
+            stream=stream), S), d_buf),
+        "combine": (timer.capture(lambda i: api.moe_combine(
+            shape, sets[i].y, sets[i].ys, sets[i].lay, sets[i].w, sets[i].out, stream=stream),
+            S), c_buf)}
+    if fp8:   # the fp8 combine carries no stamps
+        del graphs["combine"]
+    n = args.launches or 2 * S
+    recs = {"dispatch": [], "combine": []}
+    for part, (g, buf) in graphs.items():
+        timer.replay_us(g)   # warm-up
+        for _ in range(n):
+            buf.zero_()
+            timer.replay_us(g)
+            recs[part].append(buf.view(-1, 8).cpu().numpy())
+    assert lib.moe_trace_set_dispatch(None, 0) == 0
+    assert lib.moe_trace_set_combine(None, 0) == 0
+    return {"workload": w.name, "launches": n, "sets": S,
+            "timeline": {
+                "dispatch": timeline_summary(recs["dispatch"], TRACE_PHASES["dispatch"],
+                                             first_slots=4),
+                "combine": None if fp8 else timeline_summary(recs["combine"],
+                                                             TRACE_PHASES["combine"])},
+            "method": "libmoe_trace.so phase stamps (100 MHz wall clock), us from the "
+                      "launch's earliest wave entry; the last launch of each replay of a graph "
+                      "of back-to-back launches over the rotating cold sets; dispatch: "
+                      "scatter-block waves (metadata block apart); combine: one-wave blocks"}
 
 
 def dispatch_columns(w):
@@ -772,6 +913,9 @@ def main():
     from combine_moe_dispatch_amd import inputs
     w = inputs.WORKLOADS[args.workload]
     inp = inputs.generate_for(w)
+    if args.timeline:
+        print(json.dumps(run_timeline(args, w, inp)), flush=True)
+        return
     print(f"[bench] workload {w.name}: T={w.T} x {w.sources} source(s) H={w.H} E={w.E} k={w.k} N={w.N} C={w.C} "
           f"payload={w.payload}", file=sys.stderr, flush=True)
     g = run_gpu(args, w, inp)

@@ -17,6 +17,8 @@ LIB = os.path.join(HERE, "libmoe_dispatch.so")
 # streaming read/write/copy kernels for the benchmark's measured floor
 CEILING_LIB = os.path.join(HERE, "libmoe_ceiling.so")
 CEILING_SOURCE = "ceiling.hip"
+# the same sources with phase stamps (-DMOE_PHASE_STAMPS): bench.py --timeline
+TRACE_LIB = os.path.join(HERE, "libmoe_trace.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["capi.hip", "route_topk.hip", "dispatch.hip", "sources.hip", "combine.hip",
            "combine_partial.hip", "gemm_io.hip", "expert_scale.hip", "dispatch_static.hip"]
@@ -34,9 +36,10 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, trace: bool = False) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + (".trace.o" if trace else ".o"))
+    extra = ["-DMOE_PHASE_STAMPS"] if trace else []
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -54,13 +57,15 @@ def _link(objs, lib: str) -> None:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = SOURCES + [CEILING_SOURCE]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    _link(objs[:-1], LIB)
-    _link(objs[-1:], CEILING_LIB)
+    jobs = [(src, False) for src in SOURCES + [CEILING_SOURCE]] + [(src, True) for src in SOURCES]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:n + 1], CEILING_LIB)
+    _link(objs[n + 1:], TRACE_LIB)
     if verbose:
-        print("built", LIB, "and", CEILING_LIB)
+        print("built", LIB, CEILING_LIB, "and", TRACE_LIB)
     return LIB
 
 

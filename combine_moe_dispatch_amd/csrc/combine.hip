@@ -25,6 +25,12 @@ namespace {
 constexpr int kBlock = 64;  // one wavefront per block
 constexpr int kGroup = 8;   // gathers in flight per thread
 
+#ifdef MOE_PHASE_STAMPS
+// the combine kernels' trace buffer (tracing library only)
+__device__ uint64_t* g_trace;
+__device__ uint32_t g_trace_slots;
+#endif
+
 // Fold n gathered rows into acc with fp32 fused multiply-adds in slot order.
 template <int N>
 __device__ __forceinline__ void fold_rows(float (&acc)[8], const uint4 (&yv)[N],
@@ -57,6 +63,8 @@ combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ tok
                     const float* __restrict__ w, uint4* __restrict__ out, int H, int k_rt,
                     int token_major) {
   static_assert(K <= kGroup, "compile-time top-k is gathered in one group");
+  MOE_STAMP(t_entry);
+  MOE_STAMP_DECL(t_issued);
   const int k = K > 0 ? K : k_rt;
   const int t = token_major ? blockIdx.x : blockIdx.y;
   const int nvec = H / 8;
@@ -86,6 +94,7 @@ combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ tok
     for (int g = 0; g < kGroup; ++g)
       yv[g] = j0 + g < k ? load_stream(&y[(size_t)max(row[g], 0) * nvec + vc])
                          : make_uint4(0, 0, 0, 0);
+    MOE_STAMP_SET(t_issued);
     fold_rows<kGroup>(acc, yv, row, wj);
     // every gathered value is consumed on every path, so no load is moved
     // into the fold's per-row branches
@@ -93,6 +102,7 @@ combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ tok
     for (int g = 0; g < kGroup; ++g)
       if (j0 + g < k) asm volatile("" ::"v"(yv[g].x));
   }
+  MOE_STAMP(t_folded);
   if (!active) return;
   uint4 o;
   o.x = pack_bf16x2(acc[0], acc[1]);
@@ -103,6 +113,13 @@ combine_bf16_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ tok
     store_device_scope(out + (size_t)t * nvec, nvec * 16, v * 16, o);
   else
     store_stream(&out[(size_t)t * nvec + v], o);
+#ifdef MOE_PHASE_STAMPS
+  MOE_STAMP(t_stored);
+  MOE_TRACE_WAIT();
+  MOE_STAMP(t_done);
+  trace_record(g_trace, g_trace_slots, blockIdx.y * gridDim.x + blockIdx.x, t_entry, t_issued,
+               t_folded, t_folded, t_stored, t_done);
+#endif
 }
 
 // fp8: a lane owns two 8-code vectors, u and u + 64 of its block's 128, so
@@ -228,3 +245,14 @@ hipError_t launch_combine(const void* y, const float* ys, const int32_t* token_r
 }
 
 }  // namespace moe
+
+#ifdef MOE_PHASE_STAMPS
+// Tracing library only: the buffer the bf16 combine kernel writes its phase
+// records to (slots records of kTraceWords words, one per one-wave block in
+// grid order), or null to stop.  Returns 0 or the HIP error code.
+extern "C" int moe_trace_set_combine(void* buf, uint32_t slots) {
+  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(moe::g_trace), &buf, sizeof(buf));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(moe::g_trace_slots), &slots, sizeof(slots));
+  return (int)e;
+}
+#endif

@@ -157,6 +157,44 @@ constexpr unsigned kWaitVm0 = 0x0F70;
 // the branch makes them part of the first batch of argument loads.
 #define MOE_ARGS_UP_FRONT(...) asm volatile("" ::__VA_ARGS__)
 
+// Phase stamps, compiled only into the tracing library (libmoe_trace.so,
+// built with -DMOE_PHASE_STAMPS; the product library has none of this): a
+// kernel reads the 100 MHz wall clock at named points of its path, and one
+// lane per wave writes the wave's record of kTraceWords words to the trace
+// buffer its source file holds (set with that file's moe_trace_set_* call),
+// at the wave's slot when the slot fits.  MOE_TRACE_WAIT makes the wave wait
+// for its own outstanding memory operations, so that a stamp after it marks
+// their completion.
+constexpr int kTraceWords = 8;
+#ifdef MOE_PHASE_STAMPS
+#define MOE_STAMP(var) const uint64_t var = __builtin_amdgcn_s_memrealtime()
+#define MOE_STAMP_DECL(var) uint64_t var = 0
+#define MOE_STAMP_SET(var) var = __builtin_amdgcn_s_memrealtime()
+#define MOE_TRACE_WAIT() asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory")
+// lane 0 writes (w0..w5, the wave's hardware id) at record `slot`
+__device__ __forceinline__ void trace_record(uint64_t* buf, uint32_t slots, uint32_t slot,
+                                             uint64_t w0, uint64_t w1, uint64_t w2, uint64_t w3,
+                                             uint64_t w4, uint64_t w5) {
+  if (buf == nullptr || slot >= slots || (threadIdx.x & (kWave - 1)) != 0) return;
+  uint32_t hw;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+  uint64_t* r = buf + (size_t)slot * kTraceWords;
+  r[0] = w0;
+  r[1] = w1;
+  r[2] = w2;
+  r[3] = w3;
+  r[4] = w4;
+  r[5] = w5;
+  r[6] = hw;
+  r[7] = 1;  // record written
+}
+#else
+#define MOE_STAMP(var)
+#define MOE_STAMP_DECL(var)
+#define MOE_STAMP_SET(var)
+#define MOE_TRACE_WAIT()
+#endif
+
 // n / d without a division, for any n < 2^32 and d >= 1: with
 // m = floor((2^32 - 1) / d), umulhi(n, m) is floor(n / d) or one less (the
 // product undershoots n / d by less than n / 2^32 < 1), and one remainder

@@ -53,6 +53,12 @@ constexpr int kDevCapacity = 1;
 constexpr int kDevBadId = 2;
 constexpr int kComputeUnits = 256;  // MI355X
 
+#ifdef MOE_PHASE_STAMPS
+// the dispatch kernels' trace buffer (tracing library only)
+__device__ uint64_t* g_trace;
+__device__ uint32_t g_trace_slots;
+#endif
+
 // Exclusive scan of n <= kMaxExperts LDS counts into excl[0..n] (excl[n] is
 // the total).  All threads of the block must call it.
 __device__ void block_exclusive_scan(const int* cnt, int n, int* excl, int* wave_tot) {
@@ -365,6 +371,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   MOE_ARGS_UP_FRONT("s"(p.x), "s"(p.col_chunks), "s"(p.cc_magic), "s"(p.vec_per_chunk), "s"(p.H));
 
   if (blockIdx.x == 0) {
+    MOE_STAMP(t_entry0);
     // histogram, scan and the global metadata; all id loads are issued
     // before the first one is used
     int idv[IPT];
@@ -386,9 +393,17 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
     bad = __syncthreads_or(bad);
     block_exclusive_scan(s_a, p.E, s_b, s_wave);
     write_metadata(p, s_a, s_b, bad);
+#ifdef MOE_PHASE_STAMPS
+    MOE_STAMP(t_issued0);
+    MOE_TRACE_WAIT();
+    MOE_STAMP(t_done0);
+    trace_record(g_trace, g_trace_slots, threadIdx.x / kWave, t_entry0, t_entry0, t_entry0,
+                 t_entry0, t_issued0, t_done0);
+#endif
     return;
   }
 
+  MOE_STAMP(t_entry);
   // issue every load first: the whole id list (a few per thread; these do
   // not depend on the block's token), this token's k ids and this block's
   // slice of the token row
@@ -415,6 +430,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   // LDS-only barriers from here on: the slice of x loaded above stays in
   // flight while the histogram is built
   lds_barrier();
+  MOE_STAMP(t_clear);
   const int first_pos = t * p.k;
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
@@ -426,6 +442,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   const bool valid = lane < p.k && (unsigned)my_e < (unsigned)p.E;
   const int dup = earlier_same_slots(valid ? my_e + 1 : 0, lane, p.k);
   lds_barrier();
+  MOE_STAMP(t_hist);
 
   // Lane j, for its slot's expert e:
   //   B = #ids == e at positions before t*k + j (histogram of earlier tokens
@@ -466,10 +483,18 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
     }
   }
   row = checked_row(p, row);
+  MOE_STAMP(t_rows);
   // payload first: the metadata stores come after it, so the wait for the x
   // slice before the payload stores is not also a wait for them
   store_slice<PAYLOAD, MAXV>(p, u0, u1, xv, row);
   publish_rows(p, t, cc, row);
+#ifdef MOE_PHASE_STAMPS
+  MOE_STAMP(t_issued);
+  MOE_TRACE_WAIT();
+  MOE_STAMP(t_done);
+  trace_record(g_trace, g_trace_slots, blockIdx.x * kWaves + threadIdx.x / kWave, t_entry,
+               t_clear, t_hist, t_rows, t_issued, t_done);
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -757,3 +782,15 @@ hipError_t launch_dispatch(const DispatchParams& in, hipStream_t st) {
 }
 
 }  // namespace moe
+
+#ifdef MOE_PHASE_STAMPS
+// Tracing library only: the buffer the one-launch dispatch kernel writes its
+// phase records to (slots records of kTraceWords words: wave w of block b at
+// b * 4 + w; block 0 is the metadata block), or null to stop.  Returns 0 or
+// the HIP error code.
+extern "C" int moe_trace_set_dispatch(void* buf, uint32_t slots) {
+  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(moe::g_trace), &buf, sizeof(buf));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(moe::g_trace_slots), &slots, sizeof(slots));
+  return (int)e;
+}
+#endif

@@ -66,3 +66,30 @@ def test_profile_summary(tmp_path):
     assert f"| dispatch | {1024 * (900 * 2 + 14000):.0f} | 16000000 |" in out
     # event comparison: combine median 4.3 us against 4.3 us per launch
     assert "| combine | 4.300 | 4.300 | 1.000 |" in out
+
+
+def test_timeline_summary_on_synthetic_records():
+    """bench.py --timeline's summary: phases in us from each launch's earliest
+    entry (100 MHz ticks), pooled over launches, unwritten records ignored,
+    the metadata block's waves reported apart."""
+    import numpy as np
+    phases = bench.TRACE_PHASES["dispatch"]
+    recs = []
+    for launch, base in enumerate((10_000, 55_000)):
+        r = np.zeros((4 + 3, 8), np.int64)
+        # metadata block (4 waves): enters first, done at +250 ticks
+        for wv in range(4):
+            r[wv, :6] = [base, base, base, base, base + 200, base + 250]
+            r[wv, 7] = 1
+        # two scatter waves, one record left unwritten
+        r[4, :6] = base + np.array([10, 40, 70, 90, 200, 210])
+        r[5, :6] = base + np.array([30, 60, 90, 110, 260, 270])
+        r[4:6, 7] = 1
+        r[6, :6] = base + 9999   # not written (word 7 == 0): ignored
+        recs.append(r)
+    out = bench.timeline_summary(recs, phases, first_slots=4)
+    ph = out["phases_us"]
+    assert ph["entry"]["max"] == 0.3 and ph["entry"]["p50"] == 0.2
+    assert ph["rows_known"]["p50"] == 1.0 and ph["stores_done"]["max"] == 2.7
+    assert out["metadata_block_us"] == {"entry_p50": 0.0, "done_p50": 2.5, "done_max": 2.5}
+    assert out["last_done_us_p50"] == 2.7 and out["records_per_launch"] == 6
