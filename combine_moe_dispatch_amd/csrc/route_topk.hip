@@ -8,12 +8,14 @@
 // Each lane holds ceil(E/64) biased logits (coalesced: value i of lane l is
 // expert i*64 + l), packs each with its id into one 64-bit key whose unsigned
 // order is (value descending, id ascending), and sorts its keys once, best
-// first.  Each of the k rounds then takes every lane's head, finds the wave's
-// largest key with a DPP butterfly inside each 16-lane row and two DPP row
-// broadcasts across the rows (one 64-bit compare per step), and the owning
-// lane pops its head.  Equal values go to the lower expert id, so slots come
-// out in descending order.  Lanes 0..k-1 then form the weights in fp32 and
-// normalise them to one.
+// first.  Each of the k rounds then takes every lane's head and finds the
+// wave's largest key in two parts: the largest high word (the value) by a DPP
+// butterfly inside each 16-lane row and two DPP row broadcasts across the
+// rows (one max instruction per step), then a ballot of the heads holding it;
+// only when several do, the same reduction over their low words picks the
+// lowest id.  The owning lane pops its head.  Equal values go to the lower
+// expert id, so slots come out in descending order.  Lanes 0..k-1 then form
+// the weights in fp32 and normalise them to one.
 //
 // Group-limited routing (same page, MoE Router: plain top-k is the case where
 // the kept groups are all experts): each group's score is the sum of its two
@@ -32,7 +34,11 @@ namespace moe {
 
 namespace {
 
-constexpr int kRouteWaves = 4;  // tokens per 256-thread block
+// Tokens (waves) per block: one-wave blocks spread a short token list over
+// more compute units (DeepSeek-V3 decode 3.25 -> 3.02 us); four-wave blocks
+// are faster past a few thousand tokens (skewed prefill 5.16 against 5.31 us).
+constexpr int kRouteWavesLarge = 4;
+constexpr int kOneWaveMaxTokens = 2048;
 constexpr int kNone = 0x7fffffff;
 
 // (value, id) as one 64-bit key whose unsigned order is the selection order:
@@ -53,30 +59,32 @@ __device__ __forceinline__ float route_key_value(uint64_t key) {
 }
 __device__ __forceinline__ int route_key_id(uint64_t key) { return (int)~(uint32_t)key; }
 
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ void dpp_key_max(uint64_t& key) {
-  const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
-  const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWMASK, 0xf, false);
-  const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWMASK, 0xf, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  key = o > key ? o : key;
-}
-
-// Largest key over the wave (uniform result).  Four butterfly steps leave
-// every lane of a 16-lane row with the row's largest key; the row broadcasts
-// then fold row 0 into row 1 and row 2 into row 3 (lane 15 of the row
-// before), and row 1 into rows 2-3 (lane 31), so lane 63 holds the wave's
-// largest.  Keys are distinct, so the order of folding does not matter.
-__device__ __forceinline__ uint64_t wave_key_max(uint64_t key) {
-  dpp_key_max<0xB1, 0xf>(key);
-  dpp_key_max<0x4E, 0xf>(key);
-  dpp_key_max<0x141, 0xf>(key);
-  dpp_key_max<0x140, 0xf>(key);
-  dpp_key_max<0x142, 0xa>(key);
-  dpp_key_max<0x143, 0xc>(key);
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)key, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(key >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+// Largest 32-bit value over the wave (all 64 lanes active), returned
+// uniform.  Four butterfly steps leave every lane of a 16-lane row with the
+// row's largest; the row broadcasts then fold row 0 into row 1 and row 2 into
+// row 3 (lane 15 of the row before), and row 1 into rows 2-3 (lane 31), so
+// lane 63 holds the wave's largest (max is idempotent, so overlapping folds
+// do no harm).  Each step is one max instruction reading its first operand
+// through DPP, written out because the compiler's form of it is a DPP move
+// followed by the max; two wait states go before every step (a DPP read of a
+// register the previous instruction wrote) and after the last.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_max_u32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_u32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_u32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_u32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_u32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_u32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n"
+      "s_nop 1\n"
+      : "+v"(v));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Keep the two largest values seen (equal values fill both).
@@ -119,8 +127,8 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int VPL, bool GROUPED>
-__global__ void __launch_bounds__(kRouteWaves * kWave)
+template <int VPL, bool GROUPED, int WAVES>
+__global__ void __launch_bounds__(WAVES * kWave)
 route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bias, int T,
                   int E, int k, int score, int n_groups_lpg, int topk_groups,
                   int32_t* __restrict__ ids, float* __restrict__ weights) {
@@ -129,10 +137,10 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
   // Kimi-K2 shape than a separate argument)
   const int n_groups = n_groups_lpg & 0xffff;
   const int lpg = n_groups_lpg >> 16;
-  __shared__ __align__(16) float s_logit[GROUPED ? kRouteWaves : 1][GROUPED ? kMaxExperts : 1];
+  __shared__ __align__(16) float s_logit[GROUPED ? WAVES : 1][GROUPED ? kMaxExperts : 1];
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
-  const int t = blockIdx.x * kRouteWaves + wave;
+  const int t = blockIdx.x * WAVES + wave;
   // fetched with T: everything the first loads and the group step need
   if constexpr (GROUPED)
     MOE_ARGS_UP_FRONT("s"(logits), "s"(bias), "s"(n_groups_lpg), "s"(topk_groups));
@@ -279,15 +287,36 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
     }
   }
 
+  uint32_t khi[VPL], klo[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    khi[i] = (uint32_t)(key[i] >> 32);
+    klo[i] = (uint32_t)key[i];
+  }
   uint64_t my_key = 0;  // lane j keeps the key of slot j
   for (int j = 0; j < k; ++j) {
-    const uint64_t best = wave_key_max(key[0]);
-    if (best == key[0]) {  // this lane owned the winner: pop its head
-#pragma unroll
-      for (int i = 0; i + 1 < VPL; ++i) key[i] = key[i + 1];
-      key[VPL - 1] = 0ull;
+    // the largest value first; only when several heads share it, the
+    // largest low word (lowest id) among them
+    const uint32_t m = wave_max_u32(khi[0]);
+    const uint64_t tied = __ballot(khi[0] == m);
+    int win;
+    if (__popcll(tied) == 1) {
+      win = __ffsll((unsigned long long)tied) - 1;
+    } else {
+      const uint32_t ml = wave_max_u32(khi[0] == m ? klo[0] : 0u);
+      win = __ffsll((unsigned long long)__ballot(khi[0] == m && klo[0] == ml)) - 1;
     }
-    if (lane == j) my_key = best;
+    const uint32_t wl = __builtin_amdgcn_readlane(klo[0], win);
+    if (lane == win) {  // this lane owned the winner: pop its head
+#pragma unroll
+      for (int i = 0; i + 1 < VPL; ++i) {
+        khi[i] = khi[i + 1];
+        klo[i] = klo[i + 1];
+      }
+      khi[VPL - 1] = 0u;
+      klo[VPL - 1] = 0u;
+    }
+    if (lane == j) my_key = ((uint64_t)m << 32) | wl;
   }
   const float my_val = route_key_value(my_key);
   const int my_id = route_key_id(my_key);
@@ -309,25 +338,35 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
   }
 }
 
-template <int VPL>
-hipError_t launch_vpl(const float* logits, const float* bias, int T, int E, int k,
-                      int score, int n_groups, int topk_groups, int32_t* ids, float* w,
-                      hipStream_t st) {
-  const int blocks = (T + kRouteWaves - 1) / kRouteWaves;
+template <int VPL, int WAVES>
+hipError_t launch_waves(const float* logits, const float* bias, int T, int E, int k,
+                        int score, int n_groups, int topk_groups, int32_t* ids, float* w,
+                        hipStream_t st) {
+  const int blocks = (T + WAVES - 1) / WAVES;
   if (n_groups > 1 && topk_groups < n_groups) {
     // lanes per group when the groups fall on whole lanes, else 0
     const int gsz = E / n_groups;
     const int epl = (E + kWave - 1) / kWave;
     const int lpg = gsz % epl == 0 ? gsz / epl : 0;
     const bool on_lanes = lpg > 0 && lpg <= 16 && (lpg & (lpg - 1)) == 0;
-    hipLaunchKernelGGL((route_topk_kernel<VPL, true>), dim3(blocks), dim3(kRouteWaves * kWave),
-                       0, st, logits, bias, T, E, k, score,
+    hipLaunchKernelGGL((route_topk_kernel<VPL, true, WAVES>), dim3(blocks),
+                       dim3(WAVES * kWave), 0, st, logits, bias, T, E, k, score,
                        n_groups | ((on_lanes ? lpg : 0) << 16), topk_groups, ids, w);
   } else {
-    hipLaunchKernelGGL((route_topk_kernel<VPL, false>), dim3(blocks), dim3(kRouteWaves * kWave),
-                       0, st, logits, bias, T, E, k, score, 1, 1, ids, w);
+    hipLaunchKernelGGL((route_topk_kernel<VPL, false, WAVES>), dim3(blocks),
+                       dim3(WAVES * kWave), 0, st, logits, bias, T, E, k, score, 1, 1, ids, w);
   }
   return hipGetLastError();
+}
+
+template <int VPL>
+hipError_t launch_vpl(const float* logits, const float* bias, int T, int E, int k,
+                      int score, int n_groups, int topk_groups, int32_t* ids, float* w,
+                      hipStream_t st) {
+  if (T <= kOneWaveMaxTokens)
+    return launch_waves<VPL, 1>(logits, bias, T, E, k, score, n_groups, topk_groups, ids, w, st);
+  return launch_waves<VPL, kRouteWavesLarge>(logits, bias, T, E, k, score, n_groups,
+                                             topk_groups, ids, w, st);
 }
 
 }  // namespace

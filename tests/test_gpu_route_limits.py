@@ -5,7 +5,8 @@ router on every per-lane width the kernel is built for (1, 2, 4, 6, 8 and 16
 logits per lane: E in 1..64, 65..128, 129..256, 257..384, 385..512 and
 513..1024), with k past 8 (the top-k rounds beyond one DPP row of slots) and
 past 16 (the weight sum over the second row of slot lanes), and the
-group-limited router with k past 8.  Inputs: N(0,1) logits with an N(0,1)
+group-limited router with k past 8, on both block layouts (one token per
+block up to 2048 tokens, four past that).  Inputs: N(0,1) logits with an N(0,1)
 bias, and integer logits with a half-integer bias (many exact ties, which the
 selection breaks toward the lower expert id).  Bars as elsewhere: ids
 bit-exact, weights within 2^-20 relative of the oracle's double-precision
@@ -60,6 +61,10 @@ PLAIN = [
     (1000, 32, 45),
     (1024, 16, 77),
     (1024, 32, 130),
+    # past 2048 tokens: four tokens per block instead of one
+    (256, 8, 2500),
+    (384, 17, 2049),
+    (1024, 32, 2051),
 ]
 
 
@@ -88,6 +93,8 @@ GROUPED = [
     (384, 8, 2, 9, 70),      # 6 logits per lane
     (160, 8, 3, 24, 60),     # groups off whole lanes (LDS path)
     (96, 3, 2, 17, 66),
+    (256, 8, 4, 8, 2500),    # four tokens per block
+    (160, 8, 3, 9, 2049),    # four tokens per block, LDS path
 ]
 
 
@@ -102,6 +109,23 @@ def test_grouped_router_large_k(E, G, TG, k, T, ties):
         ids, w = api.moe_route_topk_grouped(d_lg, d_b, k, score, G, TG)
         torch.cuda.synchronize()
         o_ids, o_w = oracle.route_topk_grouped(lg, bias, k, score, G, TG)
+        _check(ids, w, o_ids, o_w)
+
+
+@pytest.mark.parametrize("E,k,T", [(64, 8, 40), (256, 32, 70), (1024, 16, 2100)],
+                         ids=lambda v: str(v))
+def test_router_all_values_equal(E, k, T):
+    """Every logit equal: every round's largest value is shared by every
+    lane's head, so every slot is decided by the lowest id -- experts 0..k-1
+    in order, weights all 1/k -- on the one- and four-token block layouts."""
+    print(f"[case] router all equal E={E} k={k} T={T}", flush=True)
+    lg = np.full((T, E), 0.25, np.float32)
+    d_lg = torch.from_numpy(lg).cuda()
+    for score in (api.MOE_SCORE_SIGMOID, api.MOE_SCORE_SOFTMAX):
+        ids, w = api.moe_route_topk(d_lg, None, k, score)
+        torch.cuda.synchronize()
+        o_ids, o_w = oracle.route_topk(lg, None, k, score)
+        assert np.array_equal(o_ids, np.tile(np.arange(k, dtype=np.int32), (T, 1)))
         _check(ids, w, o_ids, o_w)
 
 
