@@ -408,7 +408,7 @@ def run_gpu(args, w, inp):
         if cold and grouping is not None:
             r["route_grouped"] = timer.per_launch(on(route_grouped, sr), sr, K)
         res[mode] = r
-    if not args.no_floor and w.payload == "bf16" and w.sources == 1:
+    if not args.no_floor and w.payload == "bf16":
         res["dispatch_shape"] = dispatch_shape_floor(torch, stream, timer, w, sets[:s_disp], K)
     del sets
     torch.cuda.empty_cache()
