@@ -101,6 +101,37 @@ def test_bench_prints_one_contract_line():
     assert nx["combine_partial"]["send_us"] > 0 and nx["combine_partial"]["recv_us"] > 0
     assert nx["split"]["dispatch_recv_us"] > 0 and nx["split"]["combine_send_us"] > 0
     assert nx["route_grouped"]["route_us"] > 0
+    # the floors, with the dispatch's own grid handed its rows
+    fl = d["stream_floor"]
+    assert fl["read_us"] > 0 and fl["write_us"] > 0 and fl["empty_launch_us"] > 0
+    ds = fl["dispatch_shape"]
+    for key in ("fill_dense_us", "copy_dense_us", "fill_rows_us", "copy_rows_us"):
+        assert ds[key] > 0, key
+    assert abs(ds["dispatch_over_copy_rows"] - d["dispatch_us"] / ds["copy_rows_us"]) < 2e-3
+
+
+@pytest.mark.gpu
+def test_bench_timeline_line():
+    """bench.py --timeline (tiny workload): one JSON line with the dispatch's
+    and the combine's phases from the tracing library, percentiles ordered,
+    one record per wave of each launch."""
+    print("[case] bench.py --timeline tiny workload", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny",
+                        "--timeline", "--launches", "8"],
+                       capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert d["workload"] == "tiny" and d["launches"] == 8
+    for part, phases in bench.TRACE_PHASES.items():
+        t = d["timeline"][part]
+        got = t["phases_us"]
+        assert list(got) == [p for p in phases if not p.endswith("_")]
+        for v in got.values():
+            assert 0 <= v["p10"] <= v["p50"] <= v["p90"] <= v["max"]
+        assert t["records_per_launch"] > 0
+    assert d["timeline"]["dispatch"]["metadata_block_us"]["done_p50"] > 0
 
 
 @pytest.mark.gpu
