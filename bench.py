@@ -419,6 +419,7 @@ def run_gpu(args, w, inp):
 
 # names of the phase stamps in a trace record (words 0-5)
 TRACE_PHASES = {
+    "route": ["entry", "logits_loaded", "sorted", "selected", "stored", "done"],
     "dispatch": ["entry", "lds_cleared", "histogram", "rows_known", "stores_issued",
                  "stores_done"],
     "combine": ["entry", "gathers_issued", "folded", "folded_", "store_issued", "store_done"],
@@ -466,8 +467,8 @@ def timeline_summary(recs, phases, first_slots=0):
 
 
 def run_timeline(args, w, inp):
-    """Phase timeline of the one-launch dispatch (fused kernel, bf16 or fp8)
-    and the bf16 combine, read from libmoe_trace.so -- the library's own sources compiled
+    """Phase timeline of the router, the one-launch dispatch (fused kernel,
+    bf16 or fp8) and the bf16 combine, read from libmoe_trace.so -- the library's own sources compiled
     with -DMOE_PHASE_STAMPS, whose kernels record the 100 MHz wall clock at
     each phase of their path (the product library holds none of this).  The
     launches run back to back in HIP graphs that rotate over as many buffer
@@ -492,6 +493,7 @@ def run_timeline(args, w, inp):
         f, g = getattr(lib, name), getattr(api._lib, name)
         f.argtypes, f.restype = g.argtypes, g.restype
     vp, u32 = ctypes.c_void_p, ctypes.c_uint32
+    lib.moe_trace_set_route.argtypes = [vp, u32]
     lib.moe_trace_set_dispatch.argtypes = [vp, u32]
     lib.moe_trace_set_combine.argtypes = [vp, u32]
     api._lib = lib   # this process's binding calls now go to the tracing library
@@ -512,8 +514,11 @@ def run_timeline(args, w, inp):
     d_slots = (1 + w.tokens * -(-nvec // 256)) * 4     # the fused grid's waves, at most
     # (fp8: 16 columns a unit, so fewer blocks than this bound)
     c_slots = w.tokens * -(-nvec // 64)                 # one-wave combine blocks
+    r_slots = w.tokens                                  # one wave per token
+    r_buf = torch.zeros(r_slots * 8, dtype=torch.int64, device="cuda")
     d_buf = torch.zeros(d_slots * 8, dtype=torch.int64, device="cuda")
     c_buf = torch.zeros(c_slots * 8, dtype=torch.int64, device="cuda")
+    assert lib.moe_trace_set_route(r_buf.data_ptr(), r_slots) == 0
     assert lib.moe_trace_set_dispatch(d_buf.data_ptr(), d_slots) == 0
     assert lib.moe_trace_set_combine(c_buf.data_ptr(), c_slots) == 0
     # a graph of S back-to-back launches, one per set: each launch's records
@@ -522,6 +527,9 @@ def run_timeline(args, w, inp):
     # last used); each replay gives one launch
     timer = GraphTimer(torch, stream, 1)
     graphs = {
+        "route": (timer.capture(lambda i: api.moe_route_topk(
+            sets[i].logits, sets[i].bias, w.k, w.score, sets[i].ids, sets[i].w,
+            stream=stream), S), r_buf),
         "dispatch": (timer.capture(lambda i: api.moe_dispatch(
             shape, sets[i].x, sets[i].ids, sets[i].recv, sets[i].rs, sets[i].lay, sets[i].ws,
             stream=stream), S), d_buf),
@@ -531,17 +539,19 @@ def run_timeline(args, w, inp):
     if fp8:   # the fp8 combine carries no stamps
         del graphs["combine"]
     n = args.launches or 2 * S
-    recs = {"dispatch": [], "combine": []}
+    recs = {"route": [], "dispatch": [], "combine": []}
     for part, (g, buf) in graphs.items():
         timer.replay_us(g)   # warm-up
         for _ in range(n):
             buf.zero_()
             timer.replay_us(g)
             recs[part].append(buf.view(-1, 8).cpu().numpy())
+    assert lib.moe_trace_set_route(None, 0) == 0
     assert lib.moe_trace_set_dispatch(None, 0) == 0
     assert lib.moe_trace_set_combine(None, 0) == 0
     return {"workload": w.name, "launches": n, "sets": S,
             "timeline": {
+                "route": timeline_summary(recs["route"], TRACE_PHASES["route"]),
                 "dispatch": timeline_summary(recs["dispatch"], TRACE_PHASES["dispatch"],
                                              first_slots=4),
                 "combine": None if fp8 else timeline_summary(recs["combine"],
@@ -549,7 +559,8 @@ def run_timeline(args, w, inp):
             "method": "libmoe_trace.so phase stamps (100 MHz wall clock), us from the "
                       "launch's earliest wave entry; the last launch of each replay of a graph "
                       "of back-to-back launches over the rotating cold sets; dispatch: "
-                      "scatter-block waves (metadata block apart); combine: one-wave blocks"}
+                      "scatter-block waves (metadata block apart); combine: one-wave blocks; "
+                      "route: one wave per token"}
 
 
 def dispatch_columns(w):

@@ -41,6 +41,12 @@ constexpr int kRouteWavesLarge = 4;
 constexpr int kOneWaveMaxTokens = 2048;
 constexpr int kNone = 0x7fffffff;
 
+#ifdef MOE_PHASE_STAMPS
+// the router's trace buffer (tracing library only)
+__device__ uint64_t* g_trace;
+__device__ uint32_t g_trace_slots;
+#endif
+
 // (value, id) as one 64-bit key whose unsigned order is the selection order:
 // the high word maps the fp32 value to an order-preserving unsigned (sign bit
 // flipped for non-negative values, all bits for negative ones; -0 is taken
@@ -147,6 +153,7 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
   else
     MOE_ARGS_UP_FRONT("s"(logits), "s"(bias));
   if (t >= T) return;
+  MOE_STAMP(t_entry);
   const float* row = logits + (size_t)t * E;
 
   // Group-limited routing on whole lanes (lpg > 0, set by the host): lane l
@@ -273,6 +280,8 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
     }
   }
   // this lane's entries as keys, sorted best first (insertion network)
+  MOE_TRACE_WAIT();  // tracing only: the logits have arrived
+  MOE_STAMP(t_loaded);
   uint64_t key[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) key[i] = id[i] == kNone ? 0ull : route_key(v[i], id[i]);
@@ -293,6 +302,7 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
     khi[i] = (uint32_t)(key[i] >> 32);
     klo[i] = (uint32_t)key[i];
   }
+  MOE_STAMP(t_sorted);
   uint64_t my_key = 0;  // lane j keeps the key of slot j
   for (int j = 0; j < k; ++j) {
     // the largest value first; only when several heads share it, the
@@ -318,6 +328,7 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
     }
     if (lane == j) my_key = ((uint64_t)m << 32) | wl;
   }
+  MOE_STAMP(t_selected);
   const float my_val = route_key_value(my_key);
   const int my_id = route_key_id(my_key);
 
@@ -336,6 +347,13 @@ route_topk_kernel(const float* __restrict__ logits, const float* __restrict__ bi
     ids[(size_t)t * k + lane] = my_id;
     weights[(size_t)t * k + lane] = s / sum;
   }
+#ifdef MOE_PHASE_STAMPS
+  MOE_STAMP(t_stored);
+  MOE_TRACE_WAIT();
+  MOE_STAMP(t_done);
+  trace_record(g_trace, g_trace_slots, (uint32_t)t, t_entry, t_loaded, t_sorted, t_selected,
+               t_stored, t_done);
+#endif
 }
 
 template <int VPL, int WAVES>
@@ -387,3 +405,14 @@ hipError_t launch_route_topk(const float* logits, const float* bias, int T, int 
 }
 
 }  // namespace moe
+
+#ifdef MOE_PHASE_STAMPS
+// Tracing library only: the buffer the router writes its phase records to
+// (slots records of kTraceWords words, one per token), or null to stop.
+// Returns 0 or the HIP error code.
+extern "C" int moe_trace_set_route(void* buf, uint32_t slots) {
+  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(moe::g_trace), &buf, sizeof(buf));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(moe::g_trace_slots), &slots, sizeof(slots));
+  return (int)e;
+}
+#endif

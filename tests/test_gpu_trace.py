@@ -1,7 +1,7 @@
 """The tracing library (libmoe_trace.so: the same sources compiled with phase
 stamps, read by bench.py --timeline) computes exactly what the product library
-computes, and its one-launch dispatch and bf16 combine write one record per
-wave whose stamps are in path order.  Run through the C ABI on the GPU."""
+computes, and its router, one-launch dispatch and bf16 combine write one
+record per wave whose stamps are in path order.  Run through the C ABI on the GPU."""
 import ctypes
 import os
 
@@ -51,18 +51,22 @@ def test_tracing_library_matches_and_records_in_order():
     for name in FUNCS:
         f, g = getattr(lib, name), getattr(api._lib, name)
         f.argtypes, f.restype = g.argtypes, g.restype
+    lib.moe_trace_set_route.argtypes = [ctypes.c_void_p, ctypes.c_uint32]
     lib.moe_trace_set_dispatch.argtypes = [ctypes.c_void_p, ctypes.c_uint32]
     lib.moe_trace_set_combine.argtypes = [ctypes.c_void_p, ctypes.c_uint32]
     nvec = H // 8
     d_slots = (1 + T * -(-nvec // 256)) * 4
     c_slots = T * -(-nvec // 64)
+    r_buf = torch.zeros(T * 8, dtype=torch.int64, device="cuda")
     d_buf = torch.zeros(d_slots * 8, dtype=torch.int64, device="cuda")
     c_buf = torch.zeros(c_slots * 8, dtype=torch.int64, device="cuda")
+    assert lib.moe_trace_set_route(r_buf.data_ptr(), T) == 0
     assert lib.moe_trace_set_dispatch(d_buf.data_ptr(), d_slots) == 0
     assert lib.moe_trace_set_combine(c_buf.data_ptr(), c_slots) == 0
     try:
         traced = _run(lib, shape, inp, k)
     finally:
+        assert lib.moe_trace_set_route(None, 0) == 0
         assert lib.moe_trace_set_dispatch(None, 0) == 0
         assert lib.moe_trace_set_combine(None, 0) == 0
     plain = _run(api._lib, shape, inp, k)
@@ -76,6 +80,9 @@ def test_tracing_library_matches_and_records_in_order():
     assert written[:4].all() and blocks >= 1 + T and written[: 4 * blocks].all()
     assert not written[4 * blocks:].any()
     assert (np.diff(d[written, :6], axis=1) >= 0).all()
+    rr = r_buf.view(-1, 8).cpu().numpy()
+    assert (rr[:, 7] == 1).all()                      # one record per token
+    assert (np.diff(rr[:, :6], axis=1) >= 0).all()
     c = c_buf.view(-1, 8).cpu().numpy()
     assert (c[:, 7] == 1).all()
     assert (np.diff(c[:, [0, 1, 2, 4, 5]], axis=1) >= 0).all()
