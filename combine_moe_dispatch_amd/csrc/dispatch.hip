@@ -209,7 +209,9 @@ __device__ __forceinline__ void store_fp8(const DispatchParams& p, int u0, int u
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
           const float q0 = f[m] * r;
-          q[m] = fmaf(fmaf(-s, q0, f[m]), r, q0);
+          // a signed zero is its own quotient; the correction would turn -0
+          // into +0 (the remainder is +0, and +0 + -0 rounds to +0)
+          q[m] = f[m] == 0.0f ? f[m] : fmaf(fmaf(-s, q0, f[m]), r, q0);
         }
 #pragma unroll
         for (int w = 0; w < 4; ++w) {

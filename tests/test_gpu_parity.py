@@ -259,8 +259,9 @@ def test_fp8_decode_all_codes_through_combine():
 @pytest.mark.parametrize("T,k,payload_path", [(64, 8, "fused"), (600, 8, "chunked")])
 def test_fp8_quantiser_at_extreme_magnitudes(T, k, payload_path):
     """Blocks of 128 columns scaled by powers of two from 2^-120 to 2^120 (bf16
-    subnormals included), all-zero blocks, and blocks whose small entries
-    fall far below the smallest e4m3 step next to one large entry: codes and
+    subnormals included), all-zero and all-negative-zero blocks, signed zeros
+    beside non-zero entries, and blocks whose small entries fall far below the
+    smallest e4m3 step next to one large entry: codes and
     scales bit-exact against the oracle's IEEE division and encoder, on both
     sides of the range where the kernel divides per element instead of
     through the reciprocal."""
@@ -278,6 +279,9 @@ def test_fp8_quantiser_at_extreme_magnitudes(T, k, payload_path):
     xf[::7, 3, :] = 0.0                     # all-zero blocks
     xf[1::5, 5, :] = base[1::5, 5, :] * np.float32(2.0 ** -30)  # tiny entries beside one large one
     xf[1::5, 5, 17] = np.float32(3.0)
+    xf[2::3, 6, ::9] = np.float32(-0.0)     # signed zeros beside non-zero entries: their
+    xf[2::3, 6, 4::9] = np.float32(0.0)     # quotients are -0 and +0 (codes 0x80 and 0x00)
+    xf[::11, 7, :] = np.float32(-0.0)       # an all-negative-zero block (scale 0, codes 0)
     xb = inputs.bf16_bits_from_f32(xf.reshape(T, H))
     ids = inputs.random_ids(T, k, E, seed=4243)
     w = inputs.random_weights(T, k, seed=4244)

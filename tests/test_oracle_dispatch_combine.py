@@ -53,6 +53,8 @@ def test_quantize_fp8_matches_numpy_and_torch():
     x = inp.x_bits.copy()
     x[2, 128:256] = 0          # an all-zero block
     x[3, :128] = 0x8000        # an all-negative-zero block
+    x[4, 10] = 0x8000          # signed zeros beside non-zero entries: -0 / s = -0 (code
+    x[4, 11] = 0               # 0x80), +0 / s = +0 (code 0x00)
     for t in range(6):
         q, s = oracle.quantize_row_fp8(x[t])
         xf = (x[t].astype(np.uint32) << 16).view(np.float32).reshape(-1, 128)
