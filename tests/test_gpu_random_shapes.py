@@ -10,7 +10,10 @@ with a rank count N dividing it, k up to min(32, E), T up to 3000 (either path
 of the dispatch), packed regions or a capacity that may overflow, distinct or
 repeated experts per token, now and then ids outside [0, E), and positive
 weights.  Sizes are bounded so that the oracle checks each case in about a
-second and the receive buffer stays under 256 MB.
+second and the receive buffer stays under 256 MB.  A second set draws token
+rows with special values -- scaled by 2^e for e in [-135, 120] (bf16
+subnormals to near the fp32 limit, all finite), sprinkled with +0 and -0, or
+wholly in the bf16 subnormal range -- and now and then one expert per rank.
 """
 import numpy as np
 import pytest
@@ -70,3 +73,39 @@ def test_random_shape_chain(seed):
     shape = api.Shape(T, H, E, k, N, C, payload)
     g = run_chain(shape, inp.x_bits, inp.alpha, ids=ids, weights=wts)
     check_chain(shape, g, inp.x_bits, inp.alpha)
+
+
+def _special_rows(x_bits, rng):
+    """Finite token rows with special values (see the module docstring)."""
+    T = x_bits.shape[0]
+    xf = (x_bits.astype(np.uint32) << 16).view(np.float32).copy()
+    if T == 0:
+        return x_bits
+    mode = int(rng.integers(0, 4))
+    if mode == 1:
+        e = rng.integers(-135, 121, size=(T, 1)).astype(np.int32)
+        xf *= np.ldexp(np.float32(1), e).astype(np.float32)
+    elif mode == 2:
+        m = rng.random(xf.shape)
+        xf[m < 0.05] = np.float32(0.0)
+        xf[(m >= 0.05) & (m < 0.1)] = np.float32(-0.0)
+    elif mode == 3:
+        xf *= np.float32(2.0 ** -128)
+    return inputs.bf16_bits_from_f32(xf)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_shape_special_values(seed):
+    T, H, E, k, N, C, payload, distinct, _ = draw_case(5000 + seed)
+    rng = np.random.default_rng(6000 + seed)
+    if rng.random() < 0.15:
+        N, C = E, (int(rng.integers(1, 4)) if rng.random() < 0.5 else 0)  # one expert per rank
+    print(f"[case] random special values seed={seed} T={T} H={H} E={E} k={k} N={N} C={C} "
+          f"payload={payload}", flush=True)
+    inp = inputs.generate(T, H, E, 7000 + seed)
+    xb = _special_rows(inp.x_bits, rng)
+    ids = inputs.random_ids(T, k, E, 8000 + seed, distinct=distinct)
+    wts = inputs.random_weights(T, k, 9000 + seed)
+    shape = api.Shape(T, H, E, k, N, C, payload)
+    g = run_chain(shape, xb, inp.alpha, ids=ids, weights=wts)
+    check_chain(shape, g, xb, inp.alpha)
