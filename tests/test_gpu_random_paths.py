@@ -4,7 +4,8 @@ rows, their ranks and the output bit-exact against the oracle's fp32 chains),
 the send/receive split (both shuffles bit-exact, the split chain equal to the
 one-call chain), every source dispatching at once (layout, per-source counts
 and offsets, receive rows and the world's combine bit-exact) and the
-allocation-free dispatch (equal to moe_dispatch)."""
+allocation-free dispatch (equal to moe_dispatch); and the multi-kernel
+layout with workspaces holding arbitrary bytes."""
 import numpy as np
 import pytest
 import torch
@@ -193,3 +194,41 @@ def test_random_static_dispatch(seed):
     assert torch.equal(recv, recv2)
     if payload:
         assert torch.equal(rs.view(torch.int32), rs2.view(torch.int32))
+
+
+@pytest.mark.parametrize("fill", [0x00, 0xFF, 0x7F, 0x80])
+def test_workspace_contents_do_not_matter(fill):
+    """The multi-kernel layout's workspace needs no initialisation: filled with
+    any byte pattern before each call (and reused by the next, larger or
+    smaller, call), every result still equals the oracle's."""
+    import oracle
+    from gpu_chain import check_chain, run_chain
+    print(f"[case] workspace filled with {fill:#x}", flush=True)
+    shapes = [(1500, 256, 64, 8, 8, 0, 0), (600, 512, 32, 8, 4, 900, 1),
+              (3000, 128, 128, 4, 16, 0, 0)]
+    big = max(api.moe_dispatch_workspace_size(api.Shape(*s)) for s in shapes)
+    ws = torch.empty(big, dtype=torch.uint8, device="cuda")
+    for i, (T, H, E, k, N, C, payload) in enumerate(shapes):
+        shape = api.Shape(T, H, E, k, N, C, payload)
+        inp = inputs.generate(T, H, E, 3100 + i)
+        ids = inputs.random_ids(T, k, E, 3200 + i, distinct=(i != 1))
+        wts = inputs.random_weights(T, k, 3300 + i)
+        ws.fill_(fill)
+        x = dev_u16(inp.x_bits)
+        d_ids = torch.from_numpy(ids).cuda()
+        lay = api.Layout.empty(shape, "cuda")
+        recv, rs = api.alloc_recv(shape, "cuda", fill=0x7F if payload else 0xFFFF)
+        need = api.moe_dispatch_workspace_size(shape)
+        api.moe_dispatch(shape, x, d_ids, recv, rs, lay, ws[:need])
+        torch.cuda.synchronize()
+        o = oracle.layout(ids, E, N, C)
+        for f in ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "token_row"):
+            assert np.array_equal(getattr(lay, f).cpu().numpy().reshape(o[f].shape), o[f]), f
+        assert int(lay.status.item()) == o["status"]
+        if payload:
+            o_recv, o_rs = oracle.dispatch_fp8(inp.x_bits, o["token_row"], o["rows"], fill=0x7F)
+            assert np.array_equal(recv.cpu().numpy(), o_recv)
+            assert np.array_equal(rs.cpu().numpy().view(np.uint32), o_rs.view(np.uint32))
+        else:
+            assert np.array_equal(host_u16(recv), oracle.dispatch_bf16(inp.x_bits, o["token_row"],
+                                                                       o["rows"], fill=0xFFFF))
