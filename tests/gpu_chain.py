@@ -40,8 +40,11 @@ def _poisoned(shape: api.Shape, rows: int):
 def run_chain(shape: api.Shape, x_bits: np.ndarray, alpha: np.ndarray, *,
               logits: np.ndarray | None = None, bias: np.ndarray | None = None,
               score: int = api.MOE_SCORE_SIGMOID, ids: np.ndarray | None = None,
-              weights: np.ndarray | None = None, with_row_src: bool = True) -> dict:
-    """Everything on the GPU through the C ABI; results copied back to numpy."""
+              weights: np.ndarray | None = None, with_row_src: bool = True,
+              misalign_ids: bool = False) -> dict:
+    """Everything on the GPU through the C ABI; results copied back to numpy.
+    misalign_ids: the id list handed to dispatch starts 4 bytes past a
+    16-byte boundary (a view one element into its allocation)."""
     T, k = shape.num_tokens, shape.top_k
     out = {}
     if logits is not None:
@@ -51,6 +54,11 @@ def run_chain(shape: api.Shape, x_bits: np.ndarray, alpha: np.ndarray, *,
     else:
         d_ids = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
         d_w = torch.from_numpy(np.ascontiguousarray(weights, np.float32)).cuda()
+    if misalign_ids:
+        buf = torch.full((d_ids.numel() + 1,), -5, dtype=torch.int32, device="cuda")
+        buf[1:].copy_(d_ids.flatten())
+        d_ids = buf[1:].view(d_ids.shape)
+        assert d_ids.data_ptr() % 16 == 4
     rows = api.moe_recv_rows(shape)
     x = dev_u16(x_bits) if T > 0 else torch.empty(0, shape.hidden, dtype=torch.int16, device="cuda")
     lay = api.Layout.empty(shape, "cuda", with_row_src=with_row_src)

@@ -338,6 +338,11 @@ def test_grouped_route(T, E, G, TG, k, zipf, ties):
     (4, 128, 256, 32, 8, 4, 0, 0),
     (5, 256, 256, 48, 4, 6, 900, 0),
     (2, 100, 256, 1024, 32, 32, 0, 0),    # E and k at the library maximum, chunked
+    # 64 and 72 chunks: whole chunks per source (bases read per source), and
+    # sources that split a chunk
+    (8, 1024, 64, 256, 8, 32, 0, 0),
+    (9, 1024, 64, 256, 8, 32, 0, 0),
+    (9, 1000, 64, 64, 8, 8, 0, 0),
 ])
 def test_dispatch_sources(S, T, H, E, k, N, C, payload):
     """Every source rank dispatching at once: segments in (source, token, slot)
