@@ -43,16 +43,19 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E peak
+ONE_LAUNCH_MAX_PAIRS = 8192  # T*k up to which the library dispatches in one launch
 MALL_BYTES = 256 << 20     # Infinity Cache
 METRIC = "dispatch+combine µs and HBM GB/s (% peak), DeepSeek-V3 shape, 128 tok/rank"
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv3_decode")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="tokens per source in place of the workload's own (a fixed receive capacity is resized with them); 0 = the workload's")
     ap.add_argument("--sets", type=int, default=0, help="cold buffer sets (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -95,7 +98,7 @@ def parse():
                          "phase stamps), on rotating cold buffer sets; one JSON line")
     ap.add_argument("--launches", type=int, default=0,
                     help="with --timeline: launches read back per kernel (0 = twice the sets)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 # ---------------------------------------------------------------------------
@@ -139,9 +142,18 @@ def source_sha(part):
     return h.hexdigest()[:16]
 
 
+def workload_of(args):
+    """The workload the options name (at --tokens tokens per source if given)."""
+    from combine_moe_dispatch_amd import inputs
+    w = inputs.WORKLOADS[args.workload]
+    return inputs.with_tokens(w, args.tokens) if args.tokens else w
+
+
 def profile_tag(args):
     """Name of the committed profile that matches these options."""
     tag = args.workload
+    if args.tokens:
+        tag += f"_T{args.tokens}"
     if args.combine == "two-stage":
         tag += "_two_stage"
     if args.groups > 1:
@@ -482,10 +494,10 @@ def run_timeline(args, w, inp):
     import torch
 
     from combine_moe_dispatch_amd import api
-    if w.sources != 1 or w.tokens * w.k > 4096:
+    if w.sources != 1 or w.tokens * w.k > ONE_LAUNCH_MAX_PAIRS:
         return {"timeline": None,
-                "reason": "the trace covers the one-launch dispatch (T*k <= 4096, one "
-                          "source) and the bf16 combine"}
+                "reason": f"the trace covers the one-launch dispatch (T*k <= "
+                          f"{ONE_LAUNCH_MAX_PAIRS}, one source) and the bf16 combine"}
     fp8 = w.payload == "fp8"
     lib = ctypes.CDLL(os.path.join(ROOT, "combine_moe_dispatch_amd", "libmoe_trace.so"))
     for name in ("moe_route_topk", "moe_dispatch", "moe_expert_scale", "moe_combine",
@@ -566,12 +578,13 @@ def run_timeline(args, w, inp):
 def dispatch_columns(w):
     """(column chunks per token, 16-byte vectors per chunk) of the bf16
     dispatch's scatter grid, by its launcher's rule: on the one-launch path
-    (T*k <= 4096) up to two vectors per thread of a 256-thread block but no
-    fewer chunks than give each of the 256 compute units a block, otherwise one
-    vector per thread; chunks are whole multiples of 128 columns."""
+    (T*k <= ONE_LAUNCH_MAX_PAIRS) up to two vectors per thread of a 256-thread
+    block but no fewer chunks than give each of the 256 compute units a block,
+    otherwise one vector per thread; chunks are whole multiples of 128
+    columns."""
     nunits = w.H // 8
     ceil = lambda a, b: -(-a // b)
-    if w.tokens * w.k <= 4096:
+    if w.tokens * w.k <= ONE_LAUNCH_MAX_PAIRS:
         cc = max(ceil(nunits, 512), min(ceil(256, max(w.tokens, 1)), ceil(nunits, 256)))
     else:
         cc = ceil(nunits, 256)
@@ -789,7 +802,7 @@ def summarize_profile(args):
     options; with --write-figures also the key = value file bench.py reads."""
     import numpy as np
     from combine_moe_dispatch_amd import inputs
-    w = inputs.WORKLOADS[args.workload]
+    w = workload_of(args)
     nb = algorithmic_bytes(w)
     line = None
     if args.bench_json:
@@ -922,7 +935,7 @@ def main():
         return
 
     from combine_moe_dispatch_amd import inputs
-    w = inputs.WORKLOADS[args.workload]
+    w = workload_of(args)
     inp = inputs.generate_for(w)
     if args.timeline:
         print(json.dumps(run_timeline(args, w, inp)), flush=True)

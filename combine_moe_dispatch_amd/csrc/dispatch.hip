@@ -33,7 +33,10 @@
 //    block turns the chunk histograms into per-chunk bases and the global
 //    metadata; (3) the scatter reads a pair's row from those (for sources
 //    dispatching at once with every chunk inside one source, blocks past the
-//    scatter's also write the per-source counts and offsets).
+//    scatter's also write the per-source counts and offsets).  Up to 16
+//    chunks, (1) and (2) are one launch: each chunk's block also counts the
+//    ids of the chunks before it (its bases) and the last block writes the
+//    metadata.
 //
 // Rows move as 16-byte vectors with non-temporal (streaming) hints.  With the
 // fp8 payload a lane owns 16 columns and each group of 8 lanes one 128-column
@@ -500,33 +503,34 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
 }
 
 // ---------------------------------------------------------------------------
-// Chunked path, kernel 1: ranks inside a chunk and the chunk's histogram.
+// Chunked path: ranks inside a chunk and the chunk's counts.
 // ---------------------------------------------------------------------------
 // The chunk's 1024 pairs form 16 groups of 64 (one wave's pairs per pass), in
 // pair order.  Each wave ranks its pairs among equal experts in its group by
 // ballot matching and the group's last equal pair records the group count;
 // one pass over the groups per expert turns the counts into exclusive
-// prefixes (and the chunk total), so a pair's rank in the chunk is its
-// group's prefix plus its rank in the group.  Three barriers in all.
+// prefixes and the chunk's count of the expert (stored to count[e], global or
+// LDS), so a pair's rank in the chunk is its group's prefix plus its rank in
+// the group.  Three barriers; every thread of the block calls it.  Returns
+// whether this thread saw an id outside [0, E).
 static_assert(kChunkPairs < (1 << 16), "in-chunk prefixes are held in 16 bits");
+constexpr int kChunkSubs = kChunkPairs / kBlock;
+constexpr int kChunkGroups = kChunkSubs * kWaves;
 
-__global__ void __launch_bounds__(kBlock) layout_chunk_kernel(DispatchParams p) {
-  constexpr int kSubs = kChunkPairs / kBlock;
-  constexpr int kGroups = kSubs * kWaves;
-  // [group][expert]: counts <= 64, then prefixes <= kChunkPairs: 16 bits
-  __shared__ __align__(16) uint16_t s_grp[kGroups * kMaxExperts];
-  const int c = blockIdx.x;
+__device__ __forceinline__ bool rank_chunk(const DispatchParams& p, int c, uint16_t* s_grp,
+                                           int32_t* count) {
   const int P = p.T * p.k;
   const int E = p.E;
   const int tid = threadIdx.x;
   const int w = tid / kWave;
 
-  int idv[kSubs];
+  int idv[kChunkSubs];
 #pragma unroll
-  for (int s = 0; s < kSubs; ++s) idv[s] = p.ids[min(c * kChunkPairs + s * kBlock + tid, P - 1)];
+  for (int s = 0; s < kChunkSubs; ++s)
+    idv[s] = p.ids[min(c * kChunkPairs + s * kBlock + tid, P - 1)];
   {
     int4* g4 = reinterpret_cast<int4*>(s_grp);
-    for (int i = tid; i < kGroups * E / 8; i += kBlock) g4[i] = make_int4(0, 0, 0, 0);
+    for (int i = tid; i < kChunkGroups * E / 8; i += kBlock) g4[i] = make_int4(0, 0, 0, 0);
   }
   // LDS-only barriers: they order the histogram exchanges, not the global
   // stores of the ranks (read by a later kernel)
@@ -534,9 +538,9 @@ __global__ void __launch_bounds__(kBlock) layout_chunk_kernel(DispatchParams p) 
 
   const int bits = 32 - __clz(E);  // keys 0..E, E marks "no valid id"
   bool bad = false;
-  int before[kSubs];
+  int before[kChunkSubs];
 #pragma unroll
-  for (int s = 0; s < kSubs; ++s) {
+  for (int s = 0; s < kChunkSubs; ++s) {
     const int q = c * kChunkPairs + s * kBlock + tid;
     const bool has = q < P;
     const int e = idv[s];
@@ -550,30 +554,99 @@ __global__ void __launch_bounds__(kBlock) layout_chunk_kernel(DispatchParams p) 
   }
   lds_barrier();
   for (int e = tid; e < E; e += kBlock) {
-    int n[kGroups];
+    int n[kChunkGroups];
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) n[g] = s_grp[g * E + e];
+    for (int g = 0; g < kChunkGroups; ++g) n[g] = s_grp[g * E + e];
     int run = 0;
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
+    for (int g = 0; g < kChunkGroups; ++g) {
       s_grp[g * E + e] = (uint16_t)run;
       run += n[g];
     }
-    p.chunk_hist[(size_t)c * E + e] = run;
+    count[e] = run;
   }
   lds_barrier();
 #pragma unroll
-  for (int s = 0; s < kSubs; ++s) {
+  for (int s = 0; s < kChunkSubs; ++s) {
     const int q = c * kChunkPairs + s * kBlock + tid;
     const int e = idv[s];
     if (q < P && (unsigned)e < (unsigned)E)
       p.local_rank[q] = s_grp[(s * kWaves + w) * E + e] + before[s];
   }
-  bad = __syncthreads_or(bad);
-  if (tid == 0) p.chunk_bad[c] = bad ? 1 : 0;
+  return bad;
 }
 
-// Chunked path, kernel 2: per-chunk bases (exclusive over chunks, in place),
+// Chunked path, kernel 1 of 3: the chunk's ranks and histogram.
+__global__ void __launch_bounds__(kBlock) layout_chunk_kernel(DispatchParams p) {
+  // [group][expert]: counts <= 64, then prefixes <= kChunkPairs: 16 bits
+  __shared__ __align__(16) uint16_t s_grp[kChunkGroups * kMaxExperts];
+  const int c = blockIdx.x;
+  bool bad = rank_chunk(p, c, s_grp, p.chunk_hist + (size_t)c * p.E);
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) p.chunk_bad[c] = bad ? 1 : 0;
+}
+
+// Chunked path with at most kBaseCountMaxChunks chunks: one launch in place
+// of kernels 1 and 2.  Block c counts the ids of the chunks before it into an
+// LDS histogram, which is the chunk's base for each expert, and ranks its own
+// chunk; the last block's bases plus its own chunk's counts are the global
+// counts, from which it writes the metadata.  Block c reads c chunks of ids
+// besides its own (the last block the whole list), 16-byte loads 16 deep per
+// thread.  Up to 16 chunks that costs less than the scan launch (DeepSeek-V3
+// shape, 1536 tokens: 48.7 -> 46.9 us); at 32 chunks it costs more (4096-token
+// prefill: 106.5 -> 108.6 us), as the last block's count grows with the list.
+constexpr int kBaseCountMaxChunks = 16;
+constexpr int kCountDepth = 16;  // int4 loads in flight per thread
+
+__global__ void __launch_bounds__(kBlock) layout_bases_kernel(DispatchParams p) {
+  __shared__ __align__(16) uint16_t s_grp[kChunkGroups * kMaxExperts];
+  __shared__ int s_base[kMaxExperts];
+  __shared__ int s_own[kMaxExperts];
+  __shared__ int s_excl[kMaxExperts + 1];
+  __shared__ int s_wave[kWaves];
+  const int c = blockIdx.x;
+  const int E = p.E;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kBlock) s_base[e] = 0;
+  lds_barrier();
+
+  // the earlier chunks' ids: whole chunks, so every vector is in range
+  const int4* ids4 = reinterpret_cast<const int4*>(p.ids);
+  const int nvec = c * (kChunkPairs / 4);
+  bool bad = false;
+  for (int v0 = 0; v0 < nvec; v0 += kCountDepth * kBlock) {
+    int4 v[kCountDepth];
+#pragma unroll
+    for (int d = 0; d < kCountDepth; ++d) v[d] = ids4[min(v0 + d * kBlock + tid, nvec - 1)];
+#pragma unroll
+    for (int d = 0; d < kCountDepth; ++d) {
+      if (v0 + d * kBlock + tid < nvec) {
+        const int e4[4] = {v[d].x, v[d].y, v[d].z, v[d].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if ((unsigned)e4[i] < (unsigned)E)
+            atomicAdd(&s_base[e4[i]], 1);
+          else
+            bad = true;
+        }
+      }
+    }
+  }
+  // rank_chunk's barriers order the adds above before the reads below
+  bad |= rank_chunk(p, c, s_grp, s_own);
+  const bool last = c == p.nchunks - 1;
+  for (int e = tid; e < E; e += kBlock) {
+    const int b = s_base[e];
+    p.chunk_hist[(size_t)c * E + e] = b;
+    if (last) s_base[e] = b + s_own[e];
+  }
+  if (!last) return;  // whole block
+  bad = __syncthreads_or(bad);
+  block_exclusive_scan(s_base, E, s_excl, s_wave);
+  write_metadata(p, s_base, s_excl, bad);
+}
+
+// Chunked path, kernel 2 of 3: per-chunk bases (exclusive over chunks, in place),
 // global counts, scan and metadata.  One block; a thread per expert issues
 // the loads of 32 chunks at once.
 __global__ void __launch_bounds__(kBlock) layout_scan_kernel(DispatchParams p) {
@@ -628,7 +701,7 @@ __device__ __forceinline__ void source_metadata_from_bases(const DispatchParams&
   }
 }
 
-// Chunked path, kernel 3: rows from the chunk bases, then the scatter (and,
+// Chunked path, last kernel: rows from the chunk bases, then the scatter (and,
 // for sources dispatching at once, the per-source metadata in the blocks past
 // the scatter's).
 template <int PAYLOAD, int MAXV>
@@ -674,7 +747,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams
   publish_rows(p, t, cc, row);
 }
 
-static_assert(kSmallMaxPairs <= 16 * kBlock, "the fused path loads at most 16 ids per thread");
+static_assert(kSmallMaxPairs <= 32 * kBlock, "the fused path loads at most 32 ids per thread");
 static_assert(kSmallMaxPairs < (1 << 16), "packed histogram halves hold counts up to T*k");
 
 template <int PAYLOAD, int MAXV, int NVR>
@@ -687,8 +760,11 @@ void launch_fused(const DispatchParams& p, hipStream_t st) {
   else if (P <= kBlock * 8)
     hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 8, NVR>), dim3(blocks), dim3(kBlock),
                        0, st, p);
-  else
+  else if (P <= kBlock * 16)
     hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 16, NVR>), dim3(blocks),
+                       dim3(kBlock), 0, st, p);
+  else
+    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 32, NVR>), dim3(blocks),
                        dim3(kBlock), 0, st, p);
 }
 
@@ -704,12 +780,19 @@ hipError_t launch_paths(const DispatchParams& p, hipStream_t st) {
       launch_fused<PAYLOAD, MAXV, kDirectMaxL / 4>(p, st);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunks), dim3(kBlock), 0, st, p);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kBlock), 0, st, p);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err;
+  if (p.nchunks <= kBaseCountMaxChunks && (reinterpret_cast<uintptr_t>(p.ids) & 15) == 0) {
+    hipLaunchKernelGGL(layout_bases_kernel, dim3(p.nchunks), dim3(kBlock), 0, st, p);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  } else {
+    hipLaunchKernelGGL(layout_chunk_kernel, dim3(p.nchunks), dim3(kBlock), 0, st, p);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kBlock), 0, st, p);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL((dispatch_scatter_kernel<PAYLOAD, MAXV>),
                      dim3((unsigned)p.T * (unsigned)p.col_chunks + (unsigned)p.src_blocks),
                      dim3(kBlock), 0, st, p);

@@ -9,7 +9,7 @@ namespace moe {
 
 // Pairs up to which dispatch runs as one fused kernel: each block recounts
 // the whole id list from LDS, which stays cheap while it is this short.
-constexpr int kSmallMaxPairs = 4096;
+constexpr int kSmallMaxPairs = 8192;
 // Pairs per chunk of the multi-kernel layout path.
 constexpr int kChunkPairs = 1024;
 

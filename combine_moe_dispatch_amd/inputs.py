@@ -73,6 +73,14 @@ WORKLOADS = {
     "dsv3_world": Workload("dsv3_world", 128, 7168, 256, 8, 32, 0, SCORE_SIGMOID, "bf16",
                            "scale", 0.0, 1005, sources=32),
 }
+def with_tokens(w: Workload, T: int) -> Workload:
+    """The workload at T tokens per source; a fixed capacity is resized with
+    them (the same one-sender bound), packed regions stay packed."""
+    if T < 1:
+        raise ValueError(f"tokens must be positive, got {T}")
+    return dataclasses.replace(w, T=T, C=_cap(T, w.k, w.E, w.N) if w.C > 0 else 0)
+
+
 WORKLOAD_ORDER = ["tiny", "dsv3_decode", "kimi_k2_decode", "skewed_prefill", "fp8_payload"]
 
 

@@ -15,7 +15,7 @@
  * Then, on ids and weights drawn directly, it runs moe_dispatch and
  * moe_combine on the multi-kernel layout path (T*k above the one-kernel
  * limit, with a workspace of moe_dispatch_workspace_size bytes) for the bf16
- * and the fp8 payload, and on the one-kernel path for fp8, and checks the
+ * and the fp8 payload, and on the one-kernel path for both, and checks the
  * layout against oracle_layout, the whole poisoned receive buffer (payload,
  * fp8 scales and canary rows past the end) against oracle_dispatch_bf16 /
  * oracle_dispatch_fp8, and the output against oracle_combine_f32_ordered,
@@ -280,10 +280,22 @@ int main(void) {
   printf("c_abi_smoke: routed case (%d tokens, %d experts, top-%d, %d ranks, %lld rows) ok\n",
          T, E, K, N, (long long)rows);
   int rc;
-  /* multi-kernel layout path with a workspace: bf16 packed, fp8 with a
-     capacity some ranks overflow; then fp8 on the one-kernel path */
-  if ((rc = direct_case(700, 136, 32, 8, 4, 0, MOE_PAYLOAD_BF16, 77)) != 0) return rc;
-  if ((rc = direct_case(600, 256, 64, 8, 8, 520, MOE_PAYLOAD_FP8_E4M3_B128, 78)) != 0) return rc;
+  /* multi-kernel layout path with a workspace (more than 8192 pairs): bf16
+     packed with the layout in one launch (9 chunks of 1024 pairs) and in two
+     (17 chunks), fp8 with a capacity some ranks overflow; then the one-kernel
+     path, bf16 (5600 pairs) and fp8 */
+  {
+    const moe_shape multi = {1100, 136, 32, 8, 4, 0, MOE_PAYLOAD_BF16};
+    const moe_shape one = {700, 136, 32, 8, 4, 0, MOE_PAYLOAD_BF16};
+    if (moe_dispatch_workspace_size(&multi) == 0 || moe_dispatch_workspace_size(&one) != 0) {
+      fprintf(stderr, "workspace sizes do not follow the two dispatch paths\n");
+      return 11;
+    }
+  }
+  if ((rc = direct_case(1100, 136, 32, 8, 4, 0, MOE_PAYLOAD_BF16, 77)) != 0) return rc;
+  if ((rc = direct_case(2100, 64, 32, 8, 4, 0, MOE_PAYLOAD_BF16, 80)) != 0) return rc;
+  if ((rc = direct_case(1100, 256, 64, 8, 8, 950, MOE_PAYLOAD_FP8_E4M3_B128, 78)) != 0) return rc;
+  if ((rc = direct_case(700, 136, 32, 8, 4, 0, MOE_PAYLOAD_BF16, 81)) != 0) return rc;
   if ((rc = direct_case(64, 384, 16, 4, 4, 256, MOE_PAYLOAD_FP8_E4M3_B128, 79)) != 0) return rc;
   printf("c_abi_smoke: ok\n");
   return 0;

@@ -34,7 +34,7 @@ int main(void) {
   const moe_shape big_k = {4, 64, 64, 33, 2, 0, MOE_PAYLOAD_BF16};
   const moe_shape neg_t = {-1, 64, 8, 2, 2, 0, MOE_PAYLOAD_BF16};
   const moe_shape huge = {600000, 8, 64, 8, 8, 0, MOE_PAYLOAD_BF16};
-  const moe_shape chunked = {1000, 64, 8, 8, 2, 0, MOE_PAYLOAD_BF16};
+  const moe_shape chunked = {1100, 64, 8, 8, 2, 0, MOE_PAYLOAD_BF16};  /* 8800 pairs */
 
   expect("recv rows", (int)moe_recv_rows(&ok), 8);
   expect("recv rows of a bad shape", (int)moe_recv_rows(&e_mod_n), -1);

@@ -66,6 +66,23 @@ def test_decode_payload_matches_the_worked_size():
     assert bench.algorithmic_bytes(w)["dispatch"] - w.tokens * 8 * w.k == 16_515_072
 
 
+def test_tokens_option_resizes_the_workload():
+    """--tokens T: the named workload at T tokens per source, a fixed capacity
+    resized by the same one-sender bound, packed regions kept packed, and a
+    profile tag of its own (committed figures are for the workload's size)."""
+    args = bench.parse(["--workload", "dsv3_decode", "--tokens", "512"])
+    w = bench.workload_of(args)
+    assert (w.T, w.C, w.H, w.E, w.k, w.N) == (512, 512 * 8, 7168, 256, 8, 32)
+    assert bench.profile_tag(args) == "dsv3_decode_T512"
+    p = bench.workload_of(bench.parse(["--workload", "skewed_prefill", "--tokens", "100"]))
+    assert (p.T, p.C, p.zipf) == (100, 0, 1.2)
+    kimi = bench.workload_of(bench.parse(["--workload", "kimi_k2_decode", "--tokens", "64"]))
+    assert kimi.C == 64 * 8  # min(k, E/N) = min(8, 24)
+    assert bench.workload_of(bench.parse([])) == inputs.WORKLOADS["dsv3_decode"]
+    with pytest.raises(ValueError):
+        inputs.with_tokens(inputs.WORKLOADS["tiny"], 0)
+
+
 @pytest.mark.gpu
 def test_bench_prints_one_contract_line():
     print("[case] bench.py tiny workload", flush=True)

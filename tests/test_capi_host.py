@@ -43,6 +43,10 @@ def test_recv_rows_and_workspace():
     assert api.moe_recv_rows(S(0, 8, 1, 1, 1, 0)) == 0
     assert api.moe_dispatch_workspace_size(S(128, 7168, 256, 8, 32, 1024)) == 0
     assert api.moe_dispatch_workspace_size(S(512, 7168, 256, 8, 32, 4096, 1)) == 0
+    # one launch up to 8192 pairs, so no workspace; past that the layout's
+    assert api.moe_dispatch_workspace_size(S(1024, 7168, 256, 8, 32, 8192)) == 0
+    assert api.moe_dispatch_workspace_size(S(8192, 64, 8, 1, 1, 0)) == 0
+    assert api.moe_dispatch_workspace_size(S(1025, 7168, 256, 8, 32, 8200)) > 0
     ws = api.moe_dispatch_workspace_size(S(4096, 7168, 256, 8, 32, 0))
     assert ws >= 4 * 32768 + 4 * 32 * 256 + 4 * 32
     with pytest.raises(api.MoeError):
@@ -81,7 +85,7 @@ def test_dispatch_rejects_null_and_misaligned_pointers():
     assert f(ctypes.byref(s), 16, 16, 24, None, ctypes.byref(good), None, 0, None) == 1  # recv
     s8 = api._Shape(4, 128, 8, 2, 2, 0, 1)
     assert f(ctypes.byref(s8), 16, 16, 16, None, ctypes.byref(good), None, 0, None) == 1  # scales
-    big = api._Shape(1000, 64, 8, 8, 2, 0, 0)  # needs a workspace
+    big = api._Shape(1100, 64, 8, 8, 2, 0, 0)  # 8800 pairs: needs a workspace
     assert f(ctypes.byref(big), 16, 16, 16, None, ctypes.byref(good), None, 0, None) == 1
     assert f(ctypes.byref(big), 16, 16, 16, None, ctypes.byref(good), 16, 8, None) == 1
 
@@ -195,14 +199,19 @@ def test_stream_floor_library_loads_and_rejects_bad_arguments():
 
 def test_dispatch_columns_follow_the_launcher_rule():
     """bench.py's copy of the bf16 dispatch's column split: two chunks of 448
-    vectors at 128 tokens (256 blocks for 256 compute units), one vector per
-    thread past the one-launch limit, whole 128-column chunks."""
+    vectors at 128 tokens (256 blocks for 256 compute units) and up to the
+    one-launch limit of 8192 pairs, one vector per thread past it, whole
+    128-column chunks."""
     import bench
     from combine_moe_dispatch_amd import inputs
     W = inputs.WORKLOADS
     assert bench.dispatch_columns(W["dsv3_decode"]) == (2, 448)
     assert bench.dispatch_columns(W["skewed_prefill"]) == (4, 224)
     assert bench.dispatch_columns(W["tiny"]) == (1, 32)
+    # the one-launch path ends at 8192 pairs
+    assert bench.dispatch_columns(inputs.with_tokens(W["dsv3_decode"], 1024)) == (2, 448)
+    assert bench.dispatch_columns(inputs.with_tokens(W["dsv3_decode"], 1025)) == (4, 224)
+    assert bench.ONE_LAUNCH_MAX_PAIRS == 8192
     for w in W.values():
         cc, vpc = bench.dispatch_columns(w)
         assert vpc % 16 == 0 and cc * vpc >= w.H // 8 > (cc - 1) * vpc and vpc <= 512

@@ -1,12 +1,16 @@
-"""GPU parity of the multi-kernel layout at many chunks, and of both dispatch
-paths with an id list that does not start on a 16-byte boundary.
+"""GPU parity of the multi-kernel layout in both its forms and at many
+chunks, and of every dispatch path with an id list that does not start on a
+16-byte boundary.
 
-The multi-kernel layout ranks pairs inside chunks of 1024 (token, slot) pairs
-and carries bases across chunks; these cases reach 64 and 65 chunks (the last
-one ragged), k = 32 and one rank holding every expert.  Each case also runs
-with its id list one element into its allocation (4 bytes past a 16-byte
-boundary), which the C ABI accepts.  Every stage is checked against the oracle
-with the bars of the other parity tests."""
+The multi-kernel layout (past 8192 pairs) ranks pairs inside chunks of 1024
+(token, slot) pairs and carries bases across chunks.  Up to 16 chunks it is
+one launch whose blocks read the id list in 16-byte vectors, so a misaligned
+list takes the two-launch form instead.  These cases reach 9, 16, 17, 64 and
+65 chunks (ragged last chunks among them), k = 32 and one rank holding every
+expert, and the one-kernel path at its limit.  Each case also runs with its id
+list one element into its allocation (4 bytes past a 16-byte boundary), which
+the C ABI accepts.  Every stage is checked against the oracle with the bars of
+the other parity tests."""
 import numpy as np
 import pytest
 
@@ -21,11 +25,13 @@ CASES = [
     (8192, 64, 256, 8, 32, 0, 0, False),     # 65536 pairs: 64 chunks
     (8193, 64, 256, 8, 32, 0, 0, True),      # 65 chunks, the last one ragged
     (8192, 128, 96, 8, 3, 21000, 1, False),  # fp8, 64 chunks, a capacity that overflows
-    (513, 64, 1024, 8, 4, 0, 0, True),       # 4104 pairs: just past the one-kernel dispatch
+    (1025, 64, 1024, 8, 4, 0, 0, True),      # 8200 pairs: just past the one-kernel dispatch
+    (2000, 64, 256, 8, 32, 0, 0, True),      # 16 chunks, the last one ragged
+    (2049, 64, 256, 8, 32, 0, 0, False),     # 17 chunks
     (2048, 64, 96, 32, 3, 21000, 0, False),  # k = 32, 64 chunks, a capacity that overflows
-    (6000, 64, 8, 1, 1, 0, 0, False),        # k = 1, one rank, 6 chunks (ragged)
+    (10000, 64, 8, 1, 1, 0, 0, False),       # k = 1, one rank, 10 chunks (ragged)
     (300, 256, 256, 8, 32, 0, 0, True),      # one-kernel dispatch (2400 pairs)
-    (512, 128, 256, 8, 32, 64, 1, False),    # one-kernel fp8 dispatch at its limit (4096 pairs)
+    (1024, 128, 256, 8, 32, 64, 1, False),   # one-kernel fp8 dispatch at its limit (8192 pairs)
 ]
 
 

@@ -64,11 +64,17 @@ SWEEP = [
     (129, 1000, 64, 2, 4, 0, 0, True, None),       # ragged H/8 chunks, packed
     (200, 2056, 24, 8, 4, 0, 0, False, 5),         # duplicates and a hot expert
     (511, 384, 256, 8, 32, 0, 1, True, None),
-    (512, 256, 256, 8, 32, 4096, 0, True, None),   # 4096 pairs: fused path limit
-    (513, 256, 256, 8, 32, 4104, 0, True, None),   # first chunked case
-    (1000, 136, 8, 8, 2, 0, 0, False, 3),          # chunked, heavy duplicates
+    (512, 256, 256, 8, 32, 4096, 0, True, None),   # 4096 pairs: 16 ids per thread
+    (513, 256, 256, 8, 32, 4104, 0, True, None),   # one launch, 32 ids per thread
+    (1024, 256, 256, 8, 32, 8192, 0, True, None),  # 8192 pairs: one-launch limit
+    (1025, 256, 256, 8, 32, 8200, 0, True, None),  # first chunked case (9 chunks)
+    (2048, 256, 256, 8, 32, 0, 0, True, None),     # 16 chunks: layout in one launch
+    (2049, 256, 256, 8, 32, 0, 0, True, None),     # 17 chunks: layout in two launches
+    (1000, 136, 8, 8, 2, 0, 0, False, 3),          # one launch, heavy duplicates
+    (1100, 136, 8, 8, 2, 0, 0, False, 3),          # chunked, heavy duplicates
     (1000, 7168, 64, 1, 8, 0, 1, True, None),
-    (900, 1024, 32, 8, 4, 0, 1, False, 7),        # fp8, chunked path, duplicates
+    (900, 1024, 32, 8, 4, 0, 1, False, 7),        # fp8, one launch, duplicates
+    (1100, 1024, 32, 8, 4, 0, 1, False, 7),       # fp8, chunked path, duplicates
     (3000, 64, 1024, 8, 32, 0, 0, True, None),     # E at the library maximum
     # fixed-capacity regions on the one-launch path, with repeated experts in
     # a token: rows from the in-rank prefix (L <= 32, 16-byte and scalar
@@ -86,13 +92,18 @@ SWEEP = [
     (2048, 512, 256, 32, 256, 0, 0, True, None),   # k at the library maximum
     (64, 32768, 64, 4, 8, 0, 0, True, None),       # wide rows: 8 column chunks per token
     (40, 16384, 32, 8, 4, 320, 1, True, None),     # wide fp8 rows, 128 scale blocks
-    (700, 20480, 64, 8, 8, 0, 0, False, 1),        # wide rows on the chunked path
-    (600, 2048, 1024, 8, 64, 0, 1, True, None),    # fp8, E at the library maximum, chunked
+    (700, 20480, 64, 8, 8, 0, 0, False, 1),        # wide rows, 5600 pairs in one launch
+    (1100, 10240, 64, 8, 8, 0, 0, False, 1),       # wide rows on the chunked path
+    (600, 2048, 1024, 8, 64, 0, 1, True, None),    # fp8, E at the library maximum
+    (1100, 2048, 1024, 8, 64, 0, 1, True, None),   # the same, chunked
     (100, 1024, 512, 32, 16, 3200, 1, False, 3),   # fp8, k at the library maximum, repeats
-    # near the one-kernel limit with many blocks per compute unit: odd T,
-    # repeated experts, rows of two chunks; fp8 with capacity overflow
+    # near the 16- and 32-ids-per-thread limits of the one-kernel path with
+    # many blocks per compute unit: odd T, repeated experts, rows of two
+    # chunks; fp8 with capacity overflow
     (999, 4104, 64, 4, 8, 0, 0, False, 3),
     (1021, 256, 32, 4, 4, 1100, 1, False, 2),
+    (2047, 4104, 64, 4, 8, 0, 0, False, 3),
+    (2045, 256, 32, 4, 4, 2200, 1, False, 2),
     (70000, 8, 4, 2, 2, 0, 0, True, None),         # more tokens than a grid's y dimension holds
     (5000, 16, 8, 2, 2, 0, 0, False, None),        # combine grid just past 8192 blocks
 ]
@@ -332,11 +343,14 @@ def test_grouped_route(T, E, G, TG, k, zipf, ties):
     (4, 50, 256, 24, 4, 4, 0, 0),
     (3, 100, 256, 16, 4, 4, 160, 1),      # fixed capacity shared by all sources, overflow
     (5, 0, 64, 8, 2, 2, 8, 0),            # no tokens
-    # multi-chunk layouts: capacity overflow with fp8, the one-launch limit,
-    # ids outside [0, E)
+    # multi-chunk layouts: capacity overflow with fp8, around the one-launch
+    # limit (8192 pairs), ids outside [0, E) on both paths
     (6, 256, 512, 64, 8, 8, 1500, 1),
     (4, 128, 256, 32, 8, 4, 0, 0),
+    (8, 128, 256, 32, 8, 4, 0, 0),
+    (9, 128, 256, 32, 8, 4, 0, 0),
     (5, 256, 256, 48, 4, 6, 900, 0),
+    (5, 500, 256, 48, 4, 6, 900, 0),
     (2, 100, 256, 1024, 32, 32, 0, 0),    # E and k at the library maximum, chunked
     # 64 and 72 chunks: whole chunks per source (bases read per source), and
     # sources that split a chunk

@@ -44,7 +44,7 @@ def _inputs(T, H, E, k, seed, bad=False):
 # pairs of calls: (T, H, E, k, N, C, payload), the second smaller
 CASES = [
     ((3000, 512, 256, 8, 32, 0, 0), (700, 512, 256, 8, 32, 0, 0)),          # packed, multi-kernel
-    ((1000, 1024, 64, 8, 8, 1200, 1), (600, 1024, 64, 8, 8, 1200, 1)),      # fp8, capacity overflow
+    ((1100, 1024, 64, 8, 8, 1200, 1), (600, 1024, 64, 8, 8, 1200, 1)),      # fp8, capacity overflow
     ((8192, 256, 1024, 8, 64, 0, 0), (600, 256, 1024, 4, 64, 0, 0)),        # E at the maximum
     ((2000, 256, 32, 8, 4, 0, 0), (128, 256, 32, 8, 4, 0, 0)),              # then the one-kernel path
 ]
