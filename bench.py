@@ -772,7 +772,8 @@ def cpu_model():
 PART_KERNELS = {
     "route": ["route_topk_kernel"],
     "dispatch": ["dispatch_fused_kernel", "layout_chunk_kernel", "layout_scan_kernel",
-                 "dispatch_scatter_kernel", "source_counts_kernel", "source_offsets_kernel"],
+                 "layout_bases_kernel", "dispatch_scatter_kernel", "source_counts_kernel",
+                 "source_offsets_kernel"],
     "combine": ["combine_bf16_kernel", "combine_fp8_kernel", "combine_send_kernel",
                 "combine_send_small_kernel", "combine_recv_kernel"],
 }
