@@ -13,10 +13,12 @@ the C ABI accepts.  Every stage is checked against the oracle with the bars of
 the other parity tests."""
 import numpy as np
 import pytest
+import torch
 
+import oracle
 from combine_moe_dispatch_amd import api, inputs
 
-from gpu_chain import check_chain, run_chain
+from gpu_chain import check_chain, dev_u16, run_chain
 
 pytestmark = pytest.mark.gpu
 
@@ -51,3 +53,56 @@ def test_layout_many_chunks(case, misalign):
     shape = api.Shape(T, H, E, k, N, C, payload)
     g = run_chain(shape, inp.x_bits, inp.alpha, ids=ids, weights=wts, misalign_ids=misalign)
     check_chain(shape, g, inp.x_bits, inp.alpha)
+
+
+@pytest.mark.parametrize("T", [1100, 2100], ids=["layout_one_launch", "layout_two_launches"])
+def test_multi_kernel_dispatch_graph_replays(T):
+    """The multi-kernel dispatch (8800 pairs: layout in one launch; 16800:
+    in two) and the combine captured once in a HIP graph and replayed with
+    eager work between replays that overwrites the workspace, the layout, the
+    receive rows and the output: every replay equals the eager result, whose
+    layout equals the oracle's."""
+    H, E, k, N, C = 256, 64, 8, 8, 0
+    print(f"[case] multi-kernel dispatch graph T={T} H={H} E={E} k={k} N={N}", flush=True)
+    shape = api.Shape(T, H, E, k, N, C, api.MOE_PAYLOAD_BF16)
+    inp = inputs.generate(T, H, E, 950)
+    ids_np = inputs.random_ids(T, k, E, 951, distinct=True)
+    x = dev_u16(inp.x_bits)
+    ids = torch.from_numpy(ids_np).cuda()
+    wt = torch.from_numpy(inputs.random_weights(T, k, 952)).cuda()
+    lay = api.Layout.empty(shape, "cuda")
+    recv, _ = api.alloc_recv(shape, "cuda", fill=0)
+    ws = api.alloc_workspace(shape, "cuda")
+    assert ws is not None
+    out = torch.empty(T, H, dtype=torch.int16, device="cuda")
+
+    def step(stream=None):
+        api.moe_dispatch(shape, x, ids, recv, None, lay, ws, stream=stream)
+        api.moe_combine(shape, recv, None, lay, wt, out, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_tr, ref_recv = out.clone(), lay.token_row.clone(), recv.clone()
+    o = oracle.layout(ids_np, E, N, C)
+    assert np.array_equal(ref_tr.cpu().numpy().reshape(o["token_row"].shape), o["token_row"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(stream=s)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step(stream=s)
+    for i in range(4):
+        out.fill_(0)
+        recv.fill_(-1)
+        lay.token_row.fill_(-7)
+        lay.expert_offsets.fill_(-7)
+        ws.fill_((0x00, 0xFF, 0x7F, 0x80)[i])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lay.token_row, ref_tr), f"replay {i}: layout"
+        assert torch.equal(recv, ref_recv), f"replay {i}: receive rows"
+        assert torch.equal(out, ref_out), f"replay {i}: combine"
