@@ -25,6 +25,8 @@ ms_per_step is one replay of exactly K whole steps (route, dispatch, combine),
 synchronised on both sides.
 
 Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+[--workload NAME] [--tokens T] (T tokens per source in place of the workload's own,
+its fixed capacity resized with them).
 """
 from __future__ import annotations
 
