@@ -144,11 +144,12 @@ __device__ __forceinline__ void load_slice(const DispatchParams& p, int t, int u
 
 template <int MAXV>
 __device__ __forceinline__ void store_bf16(const DispatchParams& p, int u0, int u1,
-                                           const uint4 (&xv)[MAXV][1], int row_lane) {
+                                           const uint4 (&xv)[MAXV][1], int row_lane,
+                                           int lane0) {
   const int nvec = p.H / 8;
   uint4* recv = reinterpret_cast<uint4*>(p.recv);
   for (int j = 0; j < p.k; ++j) {
-    const int row = __builtin_amdgcn_readlane(row_lane, j);
+    const int row = __builtin_amdgcn_readlane(row_lane, lane0 + j);
     if (row < 0) continue;
     uint4* dst = recv + (size_t)row * nvec;
 #pragma unroll
@@ -174,7 +175,7 @@ __device__ __forceinline__ float lanes8_max(float v) {
 // block's scale.
 template <int MAXV>
 __device__ __forceinline__ void store_fp8(const DispatchParams& p, int u0, int u1,
-                                          const uint4 (&xv)[MAXV][2], int row_lane) {
+                                          const uint4 (&xv)[MAXV][2], int row_lane, int lane0) {
   const int nb = p.H / kFp8Block;
   const int nu = p.H / 16;
 #pragma unroll
@@ -228,7 +229,7 @@ __device__ __forceinline__ void store_fp8(const DispatchParams& p, int u0, int u
     }
     const uint4 cv = make_uint4(code[0], code[1], code[2], code[3]);
     for (int j = 0; j < p.k; ++j) {
-      const int row = __builtin_amdgcn_readlane(row_lane, j);
+      const int row = __builtin_amdgcn_readlane(row_lane, lane0 + j);
       if (row < 0) continue;
       uint4* dst = reinterpret_cast<uint4*>(p.recv) + (size_t)row * nu;
       store_stream(&dst[u], cv);
@@ -240,21 +241,23 @@ __device__ __forceinline__ void store_fp8(const DispatchParams& p, int u0, int u
   }
 }
 
+// The rows of the token's slots j = 0..k-1 are in lanes lane0 + j.
 template <int PAYLOAD, int MAXV>
 __device__ __forceinline__ void store_slice(const DispatchParams& p, int u0, int u1,
                                             const uint4 (&xv)[MAXV][Unit<PAYLOAD>::kXV],
-                                            int row_lane) {
+                                            int row_lane, int lane0 = 0) {
   if constexpr (PAYLOAD == 0)
-    store_bf16<MAXV>(p, u0, u1, xv, row_lane);
+    store_bf16<MAXV>(p, u0, u1, xv, row_lane, lane0);
   else
-    store_fp8<MAXV>(p, u0, u1, xv, row_lane);
+    store_fp8<MAXV>(p, u0, u1, xv, row_lane, lane0);
 }
 
-// Block (t, cc == 0), wave 0, lanes j < k publish the rows of token t.
-__device__ __forceinline__ void publish_rows(const DispatchParams& p, int t, int cc,
+// Blocks of column chunk 0, wave 0: lane i publishes the row of pair q0 + i,
+// for the block's n pairs.
+__device__ __forceinline__ void publish_rows(const DispatchParams& p, int q0, int n, int cc,
                                              int row_lane) {
-  if (cc == 0 && threadIdx.x < p.k) {
-    const int q = t * p.k + threadIdx.x;
+  if (cc == 0 && (int)threadIdx.x < n) {
+    const int q = q0 + threadIdx.x;
     p.token_row[q] = row_lane;
     if (p.row_src && row_lane >= 0) p.row_src[row_lane] = q;
   }
@@ -357,12 +360,16 @@ __device__ __forceinline__ int checked_row(const DispatchParams& p, int row) {
 // ---------------------------------------------------------------------------
 // Fused single-launch path.
 // ---------------------------------------------------------------------------
-// IPT = ids per thread (T*k <= IPT * kBlock).  Every global load below is
-// unconditional (indices clamped into range, values masked afterwards), so
-// the compiler can count loads in flight exactly and wait only for the ids
-// before the histograms, not for the x slice issued after them.  NVR: the
-// 16-byte vectors rank_prefix reads (at least L / 4 on its direct path).
-template <int PAYLOAD, int MAXV, int IPT, int NVR>
+// IPT = ids per thread (T*k <= IPT * kBlock).  RT = tokens per scatter
+// block: a block owns column chunk cc of the run of RT consecutive tokens
+// t0 .. t0 + RT - 1 (RT * k <= 64, so lane i of every wave holds pair
+// t0 * k + i of the run), and counts the id list once for all of them.  Every
+// global load below is unconditional (indices clamped into range, values
+// masked afterwards), so the compiler can count loads in flight exactly and
+// wait only for the ids before the histograms, not for the x slices issued
+// after them.  NVR: the 16-byte vectors rank_prefix reads (at least L / 4 on
+// its direct path).
+template <int PAYLOAD, int MAXV, int IPT, int NVR, int RT>
 __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p) {
   // histogram (packed pair in the scatter blocks), padded for rank_prefix
   __shared__ __align__(16) int s_a[kMaxExperts + kDirectMaxL];
@@ -410,48 +417,58 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
 
   MOE_STAMP(t_entry);
   // issue every load first: the whole id list (a few per thread; these do
-  // not depend on the block's token), this token's k ids and this block's
-  // slice of the token row
+  // not depend on the block's tokens), the run's ids and this block's slice
+  // of each of the run's token rows
   int idv[IPT];
 #pragma unroll
   for (int i = 0; i < IPT; ++i) idv[i] = p.ids[min(tid + i * kBlock, P - 1)];
   const int b = blockIdx.x - 1;
-  const int t = (int)udiv_magic((uint32_t)b, (uint32_t)p.col_chunks, p.cc_magic);
-  const int cc = b - t * p.col_chunks;
+  const int g = (int)udiv_magic((uint32_t)b, (uint32_t)p.col_chunks, p.cc_magic);
+  const int cc = b - g * p.col_chunks;
+  const int t0 = g * RT;
+  const int q0 = t0 * p.k;                 // the run's first pair
+  const int npairs = min(RT * p.k, P - q0);  // and its number of pairs
   const int u0 = cc * p.vec_per_chunk;
   const int u1 = min(u0 + p.vec_per_chunk, p.H >> (PAYLOAD ? 4 : 3));
-  const int my_e_raw = p.ids[t * p.k + min(lane, p.k - 1)];
-  uint4 xv[MAXV][Unit<PAYLOAD>::kXV];
-  load_slice<PAYLOAD, MAXV>(p, t, u0, u1, xv);
-  const int my_e = lane < p.k ? my_e_raw : -1;  // lane j: expert of slot j
+  const int my_e_raw = p.ids[q0 + min(lane, npairs - 1)];
+  uint4 xv[RT][MAXV][Unit<PAYLOAD>::kXV];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) load_slice<PAYLOAD, MAXV>(p, min(t0 + i, p.T - 1), u0, u1, xv[i]);
+  const int my_e = lane < npairs ? my_e_raw : -1;  // lane i: expert of pair q0 + i
 
   // Two histograms in one: s_a[e] counts all ids == e in its low 16 bits and
-  // the ids == e at positions before this token's pairs in its high 16 bits
+  // the ids == e at positions before the run's pairs in its high 16 bits
   // (T*k < 2^16, so sums of these words never carry from the low half into
   // the high half: a masked sum is a count).  s_a is cleared up to 64 whole
   // chunks, so chunk reads see zeros past E.
   const int csz = chunk_size(p.E);
   for (int e = tid; e < kWave * csz; e += kBlock) s_a[e] = 0;
-  // LDS-only barriers from here on: the slice of x loaded above stays in
+  // LDS-only barriers from here on: the slices of x loaded above stay in
   // flight while the histogram is built
   lds_barrier();
   MOE_STAMP(t_clear);
-  const int first_pos = t * p.k;
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
     const int q = tid + i * kBlock;
     const int e = idv[i];
-    if (q < P && (unsigned)e < (unsigned)p.E) atomicAdd(&s_a[e], q < first_pos ? 0x10001 : 1);
+    if (q < P && (unsigned)e < (unsigned)p.E) atomicAdd(&s_a[e], q < q0 ? 0x10001 : 1);
   }
-  // while the adds land: earlier slots of this token with the same expert
-  const bool valid = lane < p.k && (unsigned)my_e < (unsigned)p.E;
-  const int dup = earlier_same_slots(valid ? my_e + 1 : 0, lane, p.k);
+  // while the adds land: earlier pairs of the run with the same expert (one
+  // token: DPP row shifts over its k slots; a run: ballot matching)
+  const bool valid = lane < npairs && (unsigned)my_e < (unsigned)p.E;
+  int dup;
+  if constexpr (RT == 1) {
+    dup = earlier_same_slots(valid ? my_e + 1 : 0, lane, p.k);
+  } else {
+    const uint32_t key = valid ? (uint32_t)my_e : (uint32_t)p.E;
+    dup = popc64(wave_match(key, 32 - __clz(p.E)) & lanes_below());
+  }
   lds_barrier();
   MOE_STAMP(t_hist);
 
-  // Lane j, for its slot's expert e:
-  //   B = #ids == e at positions before t*k + j (histogram of earlier tokens
-  //       plus this token's earlier slots);
+  // Lane i, for the expert e of pair q = q0 + i:
+  //   B = #ids == e at positions before q (histogram of the pairs before the
+  //       run plus the run's earlier pairs);
   //   fixed-capacity regions: the row is r*C + #ids in [first, e) + B, where
   //       first is the first expert of e's rank r -- with L <= kDirectMaxL a
   //       direct sum over the rank's counts;
@@ -490,9 +507,13 @@ __global__ void __launch_bounds__(kBlock) dispatch_fused_kernel(DispatchParams p
   row = checked_row(p, row);
   MOE_STAMP(t_rows);
   // payload first: the metadata stores come after it, so the wait for the x
-  // slice before the payload stores is not also a wait for them
-  store_slice<PAYLOAD, MAXV>(p, u0, u1, xv, row);
-  publish_rows(p, t, cc, row);
+  // slices before the payload stores is not also a wait for them
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    if (t0 + i >= p.T) break;
+    store_slice<PAYLOAD, MAXV>(p, u0, u1, xv[i], row, i * p.k);
+  }
+  publish_rows(p, q0, npairs, cc, row);
 #ifdef MOE_PHASE_STAMPS
   MOE_STAMP(t_issued);
   MOE_TRACE_WAIT();
@@ -744,28 +765,69 @@ __global__ void __launch_bounds__(kBlock) dispatch_scatter_kernel(DispatchParams
   // payload first: the metadata stores come after it, so the wait for the x
   // slice before the payload stores is not also a wait for them
   store_slice<PAYLOAD, MAXV>(p, u0, u1, xv, row);
-  publish_rows(p, t, cc, row);
+  publish_rows(p, t * p.k, p.k, cc, row);
 }
 
 static_assert(kSmallMaxPairs <= 32 * kBlock, "the fused path loads at most 32 ids per thread");
 static_assert(kSmallMaxPairs < (1 << 16), "packed histogram halves hold counts up to T*k");
 
+// Runs of tokens per scatter block, only where each block recounts 32 ids per
+// thread (T*k > 4096) and a block per (token, column chunk) would put six or
+// more blocks on each compute unit: there the recount outweighs what fewer
+// blocks lose in stores in flight, as long as about two blocks per compute
+// unit remain.  Measured at the DeepSeek-V3 shape (k = 8, two column chunks):
+// 768 tokens 21.9 -> 19.9 us and 1024 tokens 29.2 -> 25.5 us with runs of 2
+// and 4, the fp8 payload at 1024 tokens 21.2 -> 16.1 us; at 513 and 600 tokens
+// (four and five blocks per compute unit) runs of two measured 2 % slower, and
+// with 16 ids per thread or fewer runs were slower throughout (fp8 payload at
+// 512 tokens 8.17 -> 8.83 us).
+constexpr int kRunsFromBlocks = 6 * kComputeUnits;
+constexpr int kFusedBlocks = 2 * kComputeUnits;
+
+// Tokens per scatter block: 1 below kRunsFromBlocks, else the most (1, 2 or
+// 4, with RT * k <= 64) that leave at least kFusedBlocks scatter blocks.
+int fused_run(const DispatchParams& p) {
+  if ((long)p.T * p.col_chunks < kRunsFromBlocks) return 1;
+  int rt = 1;
+  while (rt < 4 && 2 * rt * p.k <= kWave &&
+         (long)((p.T + 2 * rt - 1) / (2 * rt)) * p.col_chunks >= kFusedBlocks)
+    rt *= 2;
+  return rt;
+}
+
+template <int PAYLOAD, int MAXV, int IPT, int NVR>
+void launch_fused_ipt(const DispatchParams& p, hipStream_t st) {
+  if constexpr (IPT < 32) {
+    const unsigned blocks = 1u + (unsigned)p.T * (unsigned)p.col_chunks;
+    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, IPT, NVR, 1>), dim3(blocks),
+                       dim3(kBlock), 0, st, p);
+    return;
+  }
+  const int rt = fused_run(p);
+  const unsigned blocks =
+      1u + (unsigned)((p.T + rt - 1) / rt) * (unsigned)p.col_chunks;
+  if (rt == 1)
+    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, IPT, NVR, 1>), dim3(blocks),
+                       dim3(kBlock), 0, st, p);
+  else if (rt == 2)
+    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, IPT, NVR, 2>), dim3(blocks),
+                       dim3(kBlock), 0, st, p);
+  else
+    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, IPT, NVR, 4>), dim3(blocks),
+                       dim3(kBlock), 0, st, p);
+}
+
 template <int PAYLOAD, int MAXV, int NVR>
 void launch_fused(const DispatchParams& p, hipStream_t st) {
   const long P = (long)p.T * p.k;
-  const unsigned blocks = 1u + (unsigned)p.T * (unsigned)p.col_chunks;
   if (P <= kBlock * 4)
-    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 4, NVR>), dim3(blocks), dim3(kBlock),
-                       0, st, p);
+    launch_fused_ipt<PAYLOAD, MAXV, 4, NVR>(p, st);
   else if (P <= kBlock * 8)
-    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 8, NVR>), dim3(blocks), dim3(kBlock),
-                       0, st, p);
+    launch_fused_ipt<PAYLOAD, MAXV, 8, NVR>(p, st);
   else if (P <= kBlock * 16)
-    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 16, NVR>), dim3(blocks),
-                       dim3(kBlock), 0, st, p);
+    launch_fused_ipt<PAYLOAD, MAXV, 16, NVR>(p, st);
   else
-    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, 32, NVR>), dim3(blocks),
-                       dim3(kBlock), 0, st, p);
+    launch_fused_ipt<PAYLOAD, MAXV, 32, NVR>(p, st);
 }
 
 template <int PAYLOAD, int MAXV>
@@ -802,9 +864,11 @@ hipError_t launch_paths(const DispatchParams& p, hipStream_t st) {
 template <int PAYLOAD>
 hipError_t launch_payload(const DispatchParams& p, hipStream_t st) {
   const int maxv = (p.vec_per_chunk + kBlock - 1) / kBlock;
-  // column chunks hold at most two units per thread (launch_dispatch)
+  // column chunks hold at most two units per thread, and fp8 chunks one
+  // (launch_dispatch)
   if (maxv <= 1) return launch_paths<PAYLOAD, 1>(p, st);
-  if (maxv <= 2) return launch_paths<PAYLOAD, 2>(p, st);
+  if constexpr (PAYLOAD == 0)
+    if (maxv <= 2) return launch_paths<PAYLOAD, 2>(p, st);
   return hipErrorInvalidValue;
 }
 

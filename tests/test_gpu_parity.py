@@ -104,6 +104,14 @@ SWEEP = [
     (1021, 256, 32, 4, 4, 1100, 1, False, 2),
     (2047, 4104, 64, 4, 8, 0, 0, False, 3),
     (2045, 256, 32, 4, 4, 2200, 1, False, 2),
+    # runs of tokens per block on the one-launch path (32 ids per thread, six
+    # or more blocks per compute unit otherwise), ragged last runs: runs of
+    # four (packed; fp8 with a fixed capacity that overflows) and of two
+    # (bf16; fp8 with 24 experts per rank and repeats)
+    (1023, 7168, 256, 8, 32, 0, 0, False, 5),
+    (1021, 7168, 256, 8, 32, 300, 1, False, 5),
+    (769, 7168, 256, 8, 32, 0, 0, True, None),
+    (771, 7168, 384, 8, 16, 1600, 1, False, 3),
     (70000, 8, 4, 2, 2, 0, 0, True, None),         # more tokens than a grid's y dimension holds
     (5000, 16, 8, 2, 2, 0, 0, False, None),        # combine grid just past 8192 blocks
 ]
