@@ -424,6 +424,8 @@ def run_gpu(args, w, inp):
         res[mode] = r
     if not args.no_floor and w.payload == "bf16":
         res["dispatch_shape"] = dispatch_shape_floor(torch, stream, timer, w, sets[:s_disp], K)
+        if w.tokens <= 65535:
+            res["combine_shape"] = combine_shape_floor(torch, stream, timer, w, sets[:s_comb], K)
     del sets
     torch.cuda.empty_cache()
     if not args.no_floor:
@@ -627,6 +629,41 @@ def dispatch_shape_floor(torch, stream, timer, w, sets, K):
     return {"column_chunks": cc, "fill_dense_us": timed(False, False),
             "copy_dense_us": timed(True, False), "fill_rows_us": timed(False, True),
             "copy_rows_us": timed(True, True)}
+
+
+def combine_shape_floor(torch, stream, timer, w, sets, K):
+    """The bf16 combine's data movement without the weighted sum, on the
+    combine's own grid (one-wave blocks over (token, 64-vector chunk)) and the
+    same rotating sets (libmoe_ceiling's rows-gather kernel): the k 16-byte
+    gathers of each lane from rows t*k+j (one contiguous region; only where
+    those rows exist) and from the rows of the layout the dispatch wrote (its
+    rank regions, read through the token's row list like the combine), xored
+    and stored as the token's output row -- what a combine that did not fold
+    would take."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "combine_moe_dispatch_amd", "libmoe_ceiling.so"))
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.moe_ceiling_rows_gather.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    nvec = w.H // 8
+    rows_total = w.N * w.C if w.C > 0 else w.tokens * w.k
+    S = len(sets)
+    st = stream.cuda_stream
+
+    def timed(with_rows):
+        def launch(i):
+            s = sets[i % S]
+            rc = lib.moe_ceiling_rows_gather(s.y.data_ptr(),
+                                             s.lay.token_row.data_ptr() if with_rows else None,
+                                             s.out.data_ptr(), w.tokens, w.k, nvec, rows_total,
+                                             st)
+            assert rc == 0, rc
+        return timer.per_launch(launch, S, K)["us"]
+
+    timed(True)   # one discarded pass, as for the dispatch's probe
+    res = {"gather_rows_us": timed(True)}
+    if w.tokens * w.k <= rows_total:
+        res["gather_dense_us"] = timed(False)
+    return res
 
 
 def two_stage_bytes(w, partial_rows):
@@ -992,7 +1029,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": read_figure(tag, dom, "traffic_bytes_per_launch")},
+                     "traffic": read_figure(tag, dom, "traffic_bytes_per_launch"),
+                     "timing": "HIP events on the launch stream: per-launch interval of "
+                               "back-to-back launches (timing.method)"},
         "timing": {
             "method": "per launch = (t(2n) - t(n)) / n for HIP graphs of n and 2n back-to-back "
                       "launches, n a multiple of the graph's buffer sets; median and "
@@ -1013,6 +1052,14 @@ def main():
     if prof:
         # kernel durations of the committed rocprofv3 trace of these sources
         line["rocprof_kernel_trace"] = prof
+        if dom in prof:
+            # the same roofline at the profiled kernel durations (each kernel
+            # run on its own by the profiler), for reading against profiles/
+            for stat in ("median", "mean"):
+                d_us = prof[dom][f"{stat}_us"]
+                if d_us:
+                    line["roofline"][f"frac_rocprof_{stat}"] = round(
+                        nbytes[dom] / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     send_b, recv_b = two_stage_bytes(w, g["partial_rows"])
     # receive-side shuffle: each placed row read once and written once, plus
     # (counts, offsets) per expert read and the dense offsets written
@@ -1066,6 +1113,11 @@ def main():
                 "column_chunks": ds["column_chunks"],
                 **{k: round(v, 3) for k, v in ds.items() if k.endswith("_us")},
                 "dispatch_over_copy_rows": round(us["dispatch"] / ds["copy_rows_us"], 3)}
+        if "combine_shape" in g:
+            cs = g["combine_shape"]
+            line["stream_floor"]["combine_shape"] = {
+                **{k: round(v, 3) for k, v in cs.items() if k.endswith("_us")},
+                "combine_over_gather_rows": round(us["combine"] / cs["gather_rows_us"], 3)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

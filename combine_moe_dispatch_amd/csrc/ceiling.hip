@@ -1,9 +1,10 @@
 // ceiling.hip -- plain streaming kernels that measure what this GPU's memory
 // system sustains at a given size: read, write and copy of a buffer with the
 // same 16-byte non-temporal accesses the dispatch and combine kernels use, an
-// empty launch, and the dispatch's own row copy with its rows handed to it.  They are the measured floor against which the MoE
-// kernels' times are judged (libmoe_ceiling.so, used by the benchmark only;
-// not part of the dispatch/combine interface).
+// empty launch, the dispatch's own row copy with its rows handed to it, and
+// the combine's row gathers without the weighted sum.  They are the measured
+// floor against which the MoE kernels' times are judged (libmoe_ceiling.so,
+// used by the benchmark only; not part of the dispatch/combine interface).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,6 +96,39 @@ rows_copy_kernel(const u32x4* __restrict__ x, const int* __restrict__ rows,
   }
 }
 
+// The combine's data movement without its arithmetic: one-wave blocks over
+// (token, 64-vector column chunk), each lane gathering the 16-byte vector of
+// its column from the token's k rows -- rows[t*k + j] when rows is given
+// (read at uniform addresses, as the combine reads its rows), row t*k + j
+// otherwise -- with the combine's non-temporal loads and stores, and storing
+// their xor to row t of out.  The loads are unconditional (rows outside
+// [0, rows_total) read row 0 and are left out of the xor), eight at a time.
+// token_major: grid x = token, y = column chunk; otherwise the reverse.
+__global__ void __launch_bounds__(64)
+rows_gather_kernel(const u32x4* __restrict__ y, const int* __restrict__ rows,
+                   u32x4* __restrict__ out, int k, int nvec, int rows_total, int token_major) {
+  const int t = token_major ? (int)blockIdx.x : (int)blockIdx.y;
+  const int v = (token_major ? (int)blockIdx.y : (int)blockIdx.x) * 64 + (int)threadIdx.x;
+  const int vc = min(v, nvec - 1);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int r[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      r[g] = j0 + g < k ? (rows ? rows[(size_t)t * k + j0 + g] : t * k + j0 + g) : -1;
+    u32x4 val[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const bool on = r[g] >= 0 && r[g] < rows_total;
+      val[g] = __builtin_nontemporal_load(&y[(size_t)(on ? r[g] : 0) * nvec + vc]);
+      if (!on) val[g] = (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int g = 0; g < 8; ++g) acc ^= val[g];
+  }
+  if (v < nvec) __builtin_nontemporal_store(acc, &out[(size_t)t * nvec + v]);
+}
+
 __global__ void empty_kernel() {}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -159,6 +193,25 @@ extern "C" int moe_ceiling_rows_copy(const void* x, const int32_t* rows, void* d
   hipLaunchKernelGGL(rows_copy_kernel, dim3((unsigned)(T * col_chunks)), dim3(256), 0, stream,
                      static_cast<const u32x4*>(x), rows, static_cast<u32x4*>(dst), k, nvec,
                      col_chunks, vpc, rows_total);
+  return (int)hipGetLastError();
+}
+
+// y: [rows_total][nvec] 16-byte vectors; rows: [T][k] or null (rows t*k + j,
+// which must then lie below rows_total); out: [T][nvec].  Grid T x
+// ceil(nvec / 64) one-wave blocks, token-major up to 8192 blocks (as the
+// combine orders them), chunk-major past that.
+extern "C" int moe_ceiling_rows_gather(const void* y, const int32_t* rows, void* out, int T, int k,
+                                       int nvec, int rows_total, hipStream_t stream) {
+  if (!y || !out || !aligned16(y) || !aligned16(out) || T < 1 || T > 65535 || k < 1 ||
+      k > 64 || nvec < 1 || rows_total < 1 || (!rows && (long long)T * k > rows_total))
+    return 1;
+  const int chunks = (nvec + 63) / 64;
+  if (chunks > 65535) return 1;
+  const int token_major = (long long)T * chunks <= 8192 ? 1 : 0;
+  const dim3 grid = token_major ? dim3((unsigned)T, (unsigned)chunks)
+                                : dim3((unsigned)chunks, (unsigned)T);
+  hipLaunchKernelGGL(rows_gather_kernel, grid, dim3(64), 0, stream, static_cast<const u32x4*>(y),
+                     rows, static_cast<u32x4*>(out), k, nvec, rows_total, token_major);
   return (int)hipGetLastError();
 }
 

@@ -195,6 +195,15 @@ def test_stream_floor_library_loads_and_rejects_bad_arguments():
     assert rc(4096, None, 4096, 4, 2, 600, 1, 512, 8, None) == 1    # chunks miss columns
     assert rc(4096, None, 4096, 4, 2, 64, 1, 64, 7, None) == 1      # rows t*k+j past the end
     assert rc(4096, None, 4096, 0, 2, 64, 1, 64, 8, None) == 1      # no tokens
+    # the combine-shaped gather: (y, rows, out, T, k, nvec, rows_total)
+    rg = lib.moe_ceiling_rows_gather
+    rg.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    assert rg(None, None, 4096, 4, 2, 64, 8, None) == 1       # no source
+    assert rg(4096, None, 4104, 4, 2, 64, 8, None) == 1       # misaligned output
+    assert rg(4096, None, 4096, 0, 2, 64, 8, None) == 1       # no tokens
+    assert rg(4096, None, 4096, 70000, 2, 64, 140000, None) == 1  # tokens past grid y
+    assert rg(4096, None, 4096, 4, 65, 64, 260, None) == 1    # k past a wave
+    assert rg(4096, None, 4096, 4, 2, 64, 7, None) == 1       # rows t*k+j past the end
 
 
 def test_dispatch_columns_follow_the_launcher_rule():
