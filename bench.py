@@ -90,6 +90,9 @@ def parse(argv=None):
                     help="with --summarize-profile: the bench.py line of a run without the "
                          "profiler on the same sources (its algorithmic bytes and event timings "
                          "are compared with the profile)")
+    ap.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"),
+                    help="with --summarize-profile --write-figures: where the profile summary "
+                         "and figures files go")
     ap.add_argument("--write-figures", action="store_true",
                     help="with --summarize-profile: also write profiles/figures_<options>.txt")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -836,10 +839,54 @@ def _part_of(name):
     return None, None
 
 
+def bench_options(args):
+    """The bench.py options that select this workload and path."""
+    opts = f"--workload {args.workload}"
+    if args.tokens:
+        opts += f" --tokens {args.tokens}"
+    if args.groups > 1:
+        opts += f" --groups {args.groups} --topk-groups {args.topk_groups}"
+    if args.combine == "two-stage":
+        opts += " --combine two-stage"
+    if args.split:
+        opts += " --split"
+    return opts
+
+
+def profile_header(args, w):
+    """Title, workload and the commands that make a profile summary."""
+    tag, o = profile_tag(args), bench_options(args)
+    quiet = "--no-cpu-baseline --no-warm --no-next --no-floor"
+    cmds = [
+        f"python3 bench.py {o} --steps 200 --warmup 20 > bench_line.json",
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d <out>/kt -o run -- "
+        f"python3 bench.py {o} --steps 200 --warmup 20 {quiet}",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o run -- "
+        f"python3 bench.py {o} --steps 5 --warmup 2 --reps 1 {quiet}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o run -- "
+        f"python3 bench.py {o} --steps 5 --warmup 2 --reps 1 {quiet}",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/cal_fetch -o run -- "
+        "python3 bench.py --copy-calibration",
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/cal_write -o run -- "
+        "python3 bench.py --copy-calibration",
+        f"python3 bench.py --summarize-profile {o} --trace-dir <out>/kt --fetch-dir <out>/fetch "
+        f"--write-dir <out>/write --cal-fetch-dir <out>/cal_fetch --cal-write-dir "
+        f"<out>/cal_write --bench-json bench_line.json --write-figures"]
+    return [f"# {tag}: kernel durations and HBM traffic (rocprofv3, MI355X)", "",
+            f"Workload {w.name}: T={w.T} per source x {w.sources} source(s), H={w.H}, E={w.E}, "
+            f"k={w.k}, N={w.N}, C={w.C} (0 = packed), payload={w.payload}.", "",
+            "Commands, from the repository root (`cd /tmp && export TMPDIR=/tmp` first for "
+            "rocprofv3, with `bench.py` given by its full path):", ""] + \
+        [f"    {c}" for c in cmds] + [""]
+
+
 def summarize_profile(args):
     """Markdown summary of a rocprofv3 kernel trace (and optional FETCH_SIZE /
     WRITE_SIZE counter runs with their copy calibration) for this workload and
-    options; with --write-figures also the key = value file bench.py reads."""
+    options, printed; with --write-figures also written, whole (the commands
+    that make it, the --stats rows of the path's kernels, the summary and the
+    bench.py line), as <tag>_kernels_and_traffic.md, beside the key = value
+    file bench.py reads (figures_<tag>.txt), in --profiles-dir."""
     import numpy as np
     from combine_moe_dispatch_amd import inputs
     w = workload_of(args)
@@ -950,7 +997,24 @@ def summarize_profile(args):
         figures["write_scale"] = f"{wscale:.6f}"
     print("\n".join(out))
     if args.write_figures:
-        path = os.path.join(ROOT, "profiles", f"figures_{tag}.txt")
+        stats = ["| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+        srows = [r for r in _csv_rows(args.trace_dir, "kernel_stats.csv") if _part_of(r["Name"])[0]]
+        for r in sorted(srows, key=lambda r: -float(r["AverageNs"])):
+            short = r["Name"].replace("void ", "").replace("(anonymous namespace)::", "")
+            short = short.replace("moe::", "").split("(")[0]
+            stats.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                         f"{r['MinNs']} | {r['MaxNs']} |")
+        md = profile_header(args, w) + \
+            ["## rocprofv3 --stats (kernels of the path; all launches of the traced run)", ""] + \
+            stats + ["", "## Kernel trace, event timing and counters "
+                     "(bench.py --summarize-profile)", ""] + out
+        if line is not None:
+            md += ["", "## bench.py line of the same sources (no profiler)", "",
+                   "    " + json.dumps(line)]
+        os.makedirs(args.profiles_dir, exist_ok=True)
+        with open(os.path.join(args.profiles_dir, f"{tag}_kernels_and_traffic.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
+        path = os.path.join(args.profiles_dir, f"figures_{tag}.txt")
         with open(path, "w") as f:
             f.write(f"# {tag}: figures from rocprofv3 (bench.py --summarize-profile); each part's\n"
                     f"# figures hold for the kernel sources with its hash\n")

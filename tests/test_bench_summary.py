@@ -67,6 +67,34 @@ def test_profile_summary(tmp_path):
     # event comparison: combine median 4.3 us against 4.3 us per launch
     assert "| combine | 4.300 | 4.300 | 1.000 |" in out
 
+    # with --write-figures: the whole profile file and the figures file
+    _write(str(kt / "host" / "run_kernel_stats.csv"),
+           ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
+           [[names["dispatch"], 4, 21600, 5400.0, 40.0, 4000, 9000],
+            [names["combine"], 3, 12900, 4300.0, 30.0, 4100, 4500],
+            ["at::native::other_kernel", 2, 100, 50.0, 1.0, 40, 60]])
+    pdir = tmp_path / "profiles"
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-profile",
+                        "--workload", "dsv3_decode", "--groups", "8", "--topk-groups", "4",
+                        "--trace-dir", str(kt), "--bench-json", str(tmp_path / "bench.json"),
+                        "--write-figures", "--profiles-dir", str(pdir)],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    md = (pdir / "dsv3_decode_grouped_kernels_and_traffic.md").read_text()
+    assert md.startswith("# dsv3_decode_grouped: kernel durations and HBM traffic")
+    assert ("python3 bench.py --workload dsv3_decode --groups 8 --topk-groups 4 --steps 200 "
+            "--warmup 20 > bench_line.json") in md
+    # --stats rows of the path's kernels only, longest average first
+    assert "| dispatch_fused_kernel<0, 2, 4, 2> | 4 | 5400 | 4000 | 9000 |" in md
+    assert md.index("dispatch_fused_kernel<0, 2, 4, 2> | 4 |") < \
+        md.index("combine_bf16_kernel<8, false> | 3 |")
+    assert "other_kernel" not in md.split("## Kernel trace")[0]
+    assert "| dispatch | dispatch_fused_kernel | 4.300 | 5.400 | 16000000 |" in md
+    assert md.rstrip().endswith(json.dumps(json.loads((tmp_path / "bench.json").read_text())))
+    fig = (pdir / "figures_dsv3_decode_grouped.txt").read_text()
+    assert f"dispatch_source_sha = {bench.source_sha('dispatch')}" in fig
+    assert "dispatch_rocprof_median_us = 4.300" in fig
+
 
 def test_timeline_summary_on_synthetic_records():
     """bench.py --timeline's summary: phases in us from each launch's earliest
