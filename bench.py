@@ -13,7 +13,11 @@ that graph's own bytes so that the bytes it touches between two uses of a set
 exceed twice the 256 MB Infinity Cache.  Warm: one set, reused
 (cache-assisted), reported alongside.  Stream floor: plain streaming read and
 write kernels (libmoe_ceiling.so) over the payload size, timed the same way,
-give what the memory system sustains at that size.
+give what the memory system sustains at that size; one plain kernel per step
+part that reads and writes exactly that part's bytes (the dispatch: the token
+rows in, the payload out; the combine: the reverse) gives the floor the two
+kernels are judged against; copy and gather kernels on the dispatch's and the
+combine's own grids, handed their rows, give what their access patterns cost.
 
 Timing: HIP graphs of back-to-back launches replayed between HIP events on the
 launch stream.  A kernel's per-launch time is the difference of a graph of 2n
@@ -432,7 +436,8 @@ def run_gpu(args, w, inp):
     del sets
     torch.cuda.empty_cache()
     if not args.no_floor:
-        res["floor"] = stream_floor(torch, stream, timer, payload_bytes(w), K)
+        res["floor"] = stream_floor(torch, stream, timer, payload_bytes(w), K,
+                                    side_bytes=w.tokens * w.H * 2)
     return res
 
 
@@ -694,13 +699,17 @@ def payload_bytes(w):
     return w.tokens * w.k * nbytes_row(w)
 
 
-def stream_floor(torch, stream, timer, nbytes, K):
+def stream_floor(torch, stream, timer, nbytes, K, side_bytes=0):
     """What the memory system sustains at this size: plain streaming read and
     write of `nbytes` with 16-byte accesses, and an empty launch, timed like
     the kernels (graph differences over rotating buffers, cold).  Read: a
     non-temporal grid-stride loop, the best of three grid sizes.  Write: the
     best of that loop and of 64 KB blocks stored with each cache policy.
-    Copy: read and write of `nbytes` each, the non-temporal loop."""
+    Copy: read and write of `nbytes` each, the non-temporal loop.  With
+    side_bytes (the token rows: x read by the dispatch, the output written by
+    the combine), also the two kernels' own streams in one plain kernel each:
+    read side_bytes while writing nbytes (the dispatch's bytes), read nbytes
+    while writing side_bytes (the combine's), the best of three grid sizes."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "combine_moe_dispatch_amd", "libmoe_ceiling.so"))
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
@@ -709,6 +718,7 @@ def stream_floor(torch, stream, timer, nbytes, K):
     lib.moe_ceiling_write_blocked.argtypes = [vp, sz, i32, vp]
     lib.moe_ceiling_copy.argtypes = [vp, vp, sz, i32, vp]
     lib.moe_ceiling_empty.argtypes = [vp]
+    lib.moe_ceiling_read_write.argtypes = [vp, sz, vp, sz, vp, i32, vp]
     nbytes = (nbytes + 15) // 16 * 16
     S = sets_for(nbytes, 64)
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(S)]
@@ -737,10 +747,24 @@ def stream_floor(torch, stream, timer, nbytes, K):
                                                        bufs[(i + 1) % S].data_ptr(), nvec, b, st))
              for b in grids)
     em = timed(lambda i: lib.moe_ceiling_empty(st))
+    io = {}
+    if side_bytes:
+        side_bytes = (side_bytes + 15) // 16 * 16
+        sides = [torch.empty(side_bytes, dtype=torch.uint8, device="cuda") for _ in range(S)]
+        for b in sides:
+            b.fill_(1)
+        nside = side_bytes // 16
+        io["dispatch_io_us"] = min(timed(lambda i, b=b: lib.moe_ceiling_read_write(
+            sides[i % S].data_ptr(), nside, bufs[i % S].data_ptr(), nvec, sink.data_ptr(), b,
+            st)) for b in grids)
+        io["combine_io_us"] = min(timed(lambda i, b=b: lib.moe_ceiling_read_write(
+            bufs[i % S].data_ptr(), nvec, sides[i % S].data_ptr(), nside, sink.data_ptr(), b,
+            st)) for b in grids)
+        del sides
     del bufs
     torch.cuda.empty_cache()
     return {"bytes": nbytes, "sets": S, "read_us": rd, "write_us": wr, "copy_us": cp,
-            "empty_launch_us": em}
+            "empty_launch_us": em, **io}
 
 
 def cpu_baseline(w, inp, seconds):
@@ -1171,6 +1195,19 @@ def main():
             "write_plus_read_us": round(fl["write_us"] + fl["read_us"], 3),
             "dispatch_over_write_floor": round(us["dispatch"] / fl["write_us"], 3),
             "combine_over_read_floor": round(us["combine"] / fl["read_us"], 3)}
+        if "dispatch_io_us" in fl:
+            # each kernel's own streams (token rows and payload) in one plain
+            # kernel; their sum against the time the roofline fraction of
+            # `value` would need at 60 % of the peak
+            io_sum = fl["dispatch_io_us"] + fl["combine_io_us"]
+            line["stream_floor"].update({
+                "token_bytes": w.tokens * w.H * 2,
+                "dispatch_io_us": round(fl["dispatch_io_us"], 3),
+                "combine_io_us": round(fl["combine_io_us"], 3),
+                "io_floor_sum_us": round(io_sum, 3),
+                "io_floor_sum_frac": round(dc_bytes / (io_sum * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "dispatch_over_io_floor": round(us["dispatch"] / fl["dispatch_io_us"], 3),
+                "combine_over_io_floor": round(us["combine"] / fl["combine_io_us"], 3)})
         if "dispatch_shape" in g:
             ds = g["dispatch_shape"]
             line["stream_floor"]["dispatch_shape"] = {

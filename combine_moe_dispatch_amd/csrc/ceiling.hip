@@ -1,6 +1,7 @@
 // ceiling.hip -- plain streaming kernels that measure what this GPU's memory
-// system sustains at a given size: read, write and copy of a buffer with the
-// same 16-byte non-temporal accesses the dispatch and combine kernels use, an
+// system sustains at a given size: read, write and copy of a buffer, and a read
+// and a write of given sizes in one kernel, with the same 16-byte
+// non-temporal accesses the dispatch and combine kernels use, an
 // empty launch, the dispatch's own row copy with its rows handed to it, and
 // the combine's row gathers without the weighted sum.  They are the measured
 // floor against which the MoE kernels' times are judged (libmoe_ceiling.so,
@@ -30,6 +31,26 @@ stream_write_kernel(u32x4* __restrict__ p, size_t n, unsigned v) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += stride)
     __builtin_nontemporal_store(val, &p[i]);
+}
+
+// Grid-stride read of nr 16-byte vectors and write of nw in the same loop (a
+// constant stored), with the same non-temporal accesses: what a kernel that
+// only moved the bytes a dispatch (reads x, writes the rows) or a combine
+// (reads the rows, writes the output) moves would take.  The xor of what is
+// read is kept alive as in stream_read_kernel.
+__global__ void __launch_bounds__(256)
+stream_read_write_kernel(const u32x4* __restrict__ src, size_t nr, u32x4* __restrict__ dst,
+                         size_t nw, unsigned* __restrict__ sink) {
+  u32x4 acc = {0, 0, 0, 0};
+  const u32x4 val = {7u, 7u, 7u, 7u};
+  const size_t n = nr > nw ? nr : nw;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+    if (i < nr) acc ^= __builtin_nontemporal_load(&src[i]);
+    if (i < nw) __builtin_nontemporal_store(val, &dst[i]);
+  }
+  const unsigned r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (r == 0x9e3779b9u) sink[blockIdx.x] = r;
 }
 
 // Block b writes vectors [b*4096, b*4096 + 4096): 16 per thread, each
@@ -151,6 +172,19 @@ extern "C" int moe_ceiling_write(void* p, size_t nvec, int blocks, hipStream_t s
   if (!p || !aligned16(p) || blocks < 1 || blocks > 65535) return 1;
   hipLaunchKernelGGL(stream_write_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<u32x4*>(p), nvec, 7u);
+  return (int)hipGetLastError();
+}
+
+// src: nr vectors read, dst: nw vectors written (one of the two counts may be
+// 0, not both); sink: `blocks` entries.
+extern "C" int moe_ceiling_read_write(const void* src, size_t nr, void* dst, size_t nw,
+                                      void* sink, int blocks, hipStream_t stream) {
+  if ((nr && (!src || !aligned16(src))) || (nw && (!dst || !aligned16(dst))) ||
+      (nr == 0 && nw == 0) || !sink || blocks < 1 || blocks > 65535)
+    return 1;
+  hipLaunchKernelGGL(stream_read_write_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(src), nr, static_cast<u32x4*>(dst), nw,
+                     static_cast<unsigned*>(sink));
   return (int)hipGetLastError();
 }
 

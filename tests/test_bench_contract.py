@@ -125,6 +125,9 @@ def test_bench_prints_one_contract_line():
     for key in ("fill_dense_us", "copy_dense_us", "fill_rows_us", "copy_rows_us"):
         assert ds[key] > 0, key
     assert abs(ds["dispatch_over_copy_rows"] - d["dispatch_us"] / ds["copy_rows_us"]) < 2e-3
+    assert fl["dispatch_io_us"] > 0 and fl["combine_io_us"] > 0
+    assert abs(fl["io_floor_sum_us"] - fl["dispatch_io_us"] - fl["combine_io_us"]) < 2e-3
+    assert abs(fl["dispatch_over_io_floor"] - d["dispatch_us"] / fl["dispatch_io_us"]) < 2e-3
     cs = fl["combine_shape"]
     assert cs["gather_rows_us"] > 0 and cs["gather_dense_us"] > 0
     assert abs(cs["combine_over_gather_rows"] - d["combine_us"] / cs["gather_rows_us"]) < 2e-3

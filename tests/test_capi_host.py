@@ -195,6 +195,14 @@ def test_stream_floor_library_loads_and_rejects_bad_arguments():
     assert rc(4096, None, 4096, 4, 2, 600, 1, 512, 8, None) == 1    # chunks miss columns
     assert rc(4096, None, 4096, 4, 2, 64, 1, 64, 7, None) == 1      # rows t*k+j past the end
     assert rc(4096, None, 4096, 0, 2, 64, 1, 64, 8, None) == 1      # no tokens
+    # read and write of given sizes in one kernel: (src, nr, dst, nw, sink, blocks)
+    rw = lib.moe_ceiling_read_write
+    rw.argtypes = [vp, sz, vp, sz, vp, i32, vp]
+    assert rw(None, 16, 4096, 16, 256, 64, None) == 1   # reads from nowhere
+    assert rw(4096, 16, 4104, 16, 256, 64, None) == 1   # misaligned destination
+    assert rw(4096, 0, 4096, 0, 256, 64, None) == 1     # nothing to move
+    assert rw(4096, 16, 4096, 16, None, 64, None) == 1  # no sink
+    assert rw(4096, 16, 4096, 16, 256, 0, None) == 1    # no blocks
     # the combine-shaped gather: (y, rows, out, T, k, nvec, rows_total)
     rg = lib.moe_ceiling_rows_gather
     rg.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
