@@ -587,6 +587,45 @@ def run_timeline(args, w, inp):
                       "route: one wave per token"}
 
 
+def write_timeline_md(args, res):
+    """profiles/<tag>_timeline.md (in --profiles-dir): the command, the
+    method, one table of phase percentiles per kernel and the --timeline line."""
+    tag = profile_tag(args)
+    tl = res["timeline"]
+    parts = [p for p in ("route", "dispatch", "combine") if tl.get(p)]
+    names = {"route": "the router", "dispatch": "the one-launch dispatch",
+             "combine": "the bf16 combine"}
+    title = ", ".join(names[p] for p in parts[:-1]) + " and " + names[parts[-1]] \
+        if len(parts) > 1 else names[parts[0]]
+    md = [f"# {tag}: phase timeline of {title} (MI355X)", "",
+          "Command, from the repository root (libmoe_trace.so is built with the library by "
+          "`python -c \"import __graft_entry__ as g; g.build()\"`):", "",
+          f"    python3 bench.py {bench_options(args)} --timeline --write-figures", "",
+          "Microseconds from the launch's earliest wave entry, read from the phase stamps of "
+          "the tracing library (the library's sources compiled with -DMOE_PHASE_STAMPS; the "
+          "100 MHz wall clock, so 0.01 us steps). The last launch of each of "
+          f"{res['launches']} replays of a graph of {res['sets']} back-to-back launches over "
+          "the rotating cold buffer sets; percentiles over all waves of those launches. The "
+          "stamps' own waits and stores add about 0.2 us: the figures place the phases; the "
+          "kernel times are the `bench.py` line's of the same options.", ""]
+    for part in parts:
+        t = tl[part]
+        md += [f"## {part}", "", "| phase | p10 | p50 | p90 | max |", "|---|---|---|---|---|"]
+        for ph, v in t["phases_us"].items():
+            md.append(f"| {ph} | {v['p10']} | {v['p50']} | {v['p90']} | {v['max']} |")
+        extra = (f"Last wave done (median over launches): {t['last_done_us_p50']} us; "
+                 f"records per launch: {t['records_per_launch']}.")
+        if "metadata_block_us" in t:
+            m = t["metadata_block_us"]
+            extra += (f" Metadata block (block 0): entry {m['entry_p50']} us, done "
+                      f"{m['done_p50']} us (median), {m['done_max']} us (max).")
+        md += ["", extra, ""]
+    md += ["## bench.py --timeline line", "", "    " + json.dumps(res), ""]
+    os.makedirs(args.profiles_dir, exist_ok=True)
+    with open(os.path.join(args.profiles_dir, f"{tag}_timeline.md"), "w") as f:
+        f.write("\n".join(md))
+
+
 def dispatch_columns(w):
     """(column chunks per token, 16-byte vectors per chunk) of the bf16
     dispatch's scatter grid, by its launcher's rule: on the one-launch path
@@ -1066,7 +1105,10 @@ def main():
     w = workload_of(args)
     inp = inputs.generate_for(w)
     if args.timeline:
-        print(json.dumps(run_timeline(args, w, inp)), flush=True)
+        res = run_timeline(args, w, inp)
+        print(json.dumps(res), flush=True)
+        if args.write_figures and res.get("timeline"):
+            write_timeline_md(args, res)
         return
     print(f"[bench] workload {w.name}: T={w.T} x {w.sources} source(s) H={w.H} E={w.E} k={w.k} N={w.N} C={w.C} "
           f"payload={w.payload}", file=sys.stderr, flush=True)
