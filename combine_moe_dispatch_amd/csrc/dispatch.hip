@@ -801,20 +801,20 @@ void launch_fused_ipt(const DispatchParams& p, hipStream_t st) {
     const unsigned blocks = 1u + (unsigned)p.T * (unsigned)p.col_chunks;
     hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, IPT, NVR, 1>), dim3(blocks),
                        dim3(kBlock), 0, st, p);
-    return;
+  } else {  // runs are built only for 32 ids per thread
+    const int rt = fused_run(p);
+    const unsigned blocks =
+        1u + (unsigned)((p.T + rt - 1) / rt) * (unsigned)p.col_chunks;
+    if (rt == 1)
+      hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, IPT, NVR, 1>), dim3(blocks),
+                         dim3(kBlock), 0, st, p);
+    else if (rt == 2)
+      hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, IPT, NVR, 2>), dim3(blocks),
+                         dim3(kBlock), 0, st, p);
+    else
+      hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, IPT, NVR, 4>), dim3(blocks),
+                         dim3(kBlock), 0, st, p);
   }
-  const int rt = fused_run(p);
-  const unsigned blocks =
-      1u + (unsigned)((p.T + rt - 1) / rt) * (unsigned)p.col_chunks;
-  if (rt == 1)
-    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, IPT, NVR, 1>), dim3(blocks),
-                       dim3(kBlock), 0, st, p);
-  else if (rt == 2)
-    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, IPT, NVR, 2>), dim3(blocks),
-                       dim3(kBlock), 0, st, p);
-  else
-    hipLaunchKernelGGL((dispatch_fused_kernel<PAYLOAD, MAXV, IPT, NVR, 4>), dim3(blocks),
-                       dim3(kBlock), 0, st, p);
 }
 
 template <int PAYLOAD, int MAXV, int NVR>
