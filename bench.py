@@ -16,7 +16,7 @@ write kernels (libmoe_ceiling.so) over the payload size, timed the same way,
 give what the memory system sustains at that size; one plain kernel per step
 part that reads and writes exactly that part's bytes (the dispatch: the token
 rows in, the payload out; the combine: the reverse) gives the floor the two
-kernels are judged against; copy and gather kernels on the dispatch's and the
+kernels are compared with; copy and gather kernels on the dispatch's and the
 combine's own grids, handed their rows, give what their access patterns cost.
 
 Timing: HIP graphs of back-to-back launches replayed between HIP events on the

@@ -4,7 +4,7 @@
 // non-temporal accesses the dispatch and combine kernels use, an
 // empty launch, the dispatch's own row copy with its rows handed to it, and
 // the combine's row gathers without the weighted sum.  They are the measured
-// floor against which the MoE kernels' times are judged (libmoe_ceiling.so,
+// floor the MoE kernels' times are compared with (libmoe_ceiling.so,
 // used by the benchmark only; not part of the dispatch/combine interface).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
