@@ -88,6 +88,8 @@ SWEEP = [
     (100, 512, 64, 12, 8, 800, 1, False, 3),       # k = 12, fp8
     (100, 512, 64, 6, 8, 600, 0, True, None),      # k = 6 (compile-time combine)
     (100, 512, 64, 6, 8, 600, 1, False, 2),        # k = 6, fp8, repeats
+    (160, 512, 80, 8, 4, 300, 0, False, 3),        # L = 20: sums of whole vectors plus a
+    (140, 256, 112, 8, 4, 280, 1, False, 5),       # partial one (L = 28, fp8); both overflow
     (64, 256, 256, 8, 2, 512, 0, False, 9),        # L = 128
     (2048, 512, 256, 32, 256, 0, 0, True, None),   # k at the library maximum
     (64, 32768, 64, 4, 8, 0, 0, True, None),       # wide rows: 8 column chunks per token
